@@ -1,0 +1,166 @@
+"""fp64 CPU oracle for the NEO-unify generation-pass attention block.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg use it; the HIP library never imports, links or calls it, and
+it never imports the library.  The arithmetic lives in ``neo_oracle.c`` (plain
+fp64 loops, cited there against the pages); this module only marshals numpy
+arrays through ctypes.
+
+Pages cited:
+  [A] "SenseNova-U1.5 (NEO-unify) architecture" (Mobius design note)
+  [B] "SenseNova-U1: Unifying Multimodal Understanding and Generation with
+      NEO-unify Architecture" (paper notes)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "neo_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_ip = ctypes.POINTER(ctypes.c_int32)
+_lp = ctypes.POINTER(ctypes.c_int64)
+
+
+def build(force: bool = True) -> str:
+    """Compile neo_oracle.c with gcc (fp64, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC",
+               "-shared", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_split_rmsnorm.argtypes = [_dp, _dp, ctypes.c_int64, _dp, _dp, ctypes.c_double]
+        lib.oracle_rope3.argtypes = [_dp, ctypes.c_int64, ctypes.c_int64, _ip,
+                                     ctypes.c_double, ctypes.c_double]
+        lib.oracle_norm_rope.argtypes = [_dp, _dp, ctypes.c_int64, ctypes.c_int64, _dp, _dp, _ip,
+                                         ctypes.c_double, ctypes.c_double, ctypes.c_double]
+        lib.oracle_gen_attn.argtypes = [_dp, _dp, _dp, _dp, _dp, _ip, _ip, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_double, _lp, ctypes.c_int64, _dp, _dp]
+        lib.oracle_euler_step.argtypes = [_dp, _dp, ctypes.c_int64, ctypes.c_double,
+                                          ctypes.c_double, ctypes.c_double]
+        _lib = lib
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _ptr(a, typ):
+    return a.ctypes.data_as(typ)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def split_rmsnorm(x, w_t, w_hw, eps=1e-6) -> np.ndarray:
+    """Split-half RMSNorm of head rows [..., 128]; [A] §Three rotary axes."""
+    x = _f64(x)
+    assert x.shape[-1] == 128
+    y = np.empty_like(x)
+    rows = x.size // 128
+    _load().oracle_split_rmsnorm(_ptr(x, _dp), _ptr(y, _dp), rows, _ptr(_f64(w_t), _dp),
+                                 _ptr(_f64(w_hw), _dp), float(eps))
+    return y
+
+
+def rope3(x, pos, theta=5.0e6, theta_hw=1.0e4) -> np.ndarray:
+    """Three-axis half-split rotary of [T, H, 128] at positions [3, T]; [A] §Three rotary axes."""
+    y = _f64(x).copy()
+    T, H, D = y.shape
+    assert D == 128
+    pos = _i32(pos)
+    assert pos.shape == (3, T)
+    _load().oracle_rope3(_ptr(y, _dp), T, H, _ptr(pos, _ip), float(theta), float(theta_hw))
+    return y
+
+
+def norm_rope(x, w_t, w_hw, pos, theta=5.0e6, theta_hw=1.0e4, eps=1e-6) -> np.ndarray:
+    """Split-half RMSNorm followed by three-axis rotary, [T, H, 128]."""
+    x = _f64(x)
+    T, H, D = x.shape
+    assert D == 128
+    pos = _i32(pos)
+    assert pos.shape == (3, T)
+    y = np.empty_like(x)
+    _load().oracle_norm_rope(_ptr(x, _dp), _ptr(y, _dp), T, H, _ptr(_f64(w_t), _dp),
+                             _ptr(_f64(w_hw), _dp), _ptr(pos, _ip), float(theta),
+                             float(theta_hw), float(eps))
+    return y
+
+
+def qknorm_rope3(q, k, wq_t, wq_hw, wk_t, wk_hw, pos, theta=5.0e6, theta_hw=1.0e4,
+                 eps=1e-6):
+    """The generation-pass prologue on queries and the image block's keys."""
+    return (norm_rope(q, wq_t, wq_hw, pos, theta, theta_hw, eps),
+            norm_rope(k, wk_t, wk_hw, pos, theta, theta_hw, eps))
+
+
+def gen_attn(q, k_img, v_img, k_pre, v_pre, cu_q, cu_p, scale=None, tokens=None,
+             with_lse=False):
+    """Generation-pass attention over [prefix_b ; image_b]; [A] §Mixture of Transformers.
+
+    q: [Tq, Hq, D]; k_img/v_img: [Tq, Hkv, D]; k_pre/v_pre: [Tp, Hkv, D];
+    cu_q/cu_p: [B+1].  tokens: optional global query rows to evaluate.
+    Returns out [n, Hq, D] (and lse [n, Hq] when with_lse).
+    """
+    q, k_img, v_img = _f64(q), _f64(k_img), _f64(v_img)
+    k_pre, v_pre = _f64(k_pre), _f64(v_pre)
+    cu_q, cu_p = _i32(cu_q), _i32(cu_p)
+    Tq, Hq, D = q.shape
+    Hkv = k_img.shape[1]
+    B = cu_q.shape[0] - 1
+    if k_pre.size == 0:  # keep valid pointers for an empty prefix
+        k_pre = np.zeros((1, Hkv, D))
+        v_pre = np.zeros((1, Hkv, D))
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    if tokens is None:
+        tok_arr, n, tok_ptr = None, Tq, None
+    else:
+        tok_arr = np.ascontiguousarray(tokens, dtype=np.int64)
+        n = tok_arr.shape[0]
+        tok_ptr = _ptr(tok_arr, _lp)
+    out = np.zeros((max(n, 1), Hq, D))
+    lse = np.zeros((max(n, 1), Hq))
+    _load().oracle_gen_attn(_ptr(q, _dp), _ptr(k_img, _dp), _ptr(v_img, _dp), _ptr(k_pre, _dp),
+                            _ptr(v_pre, _dp), _ptr(cu_q, _ip), _ptr(cu_p, _ip), B, Hq, Hkv, D,
+                            float(scale), tok_ptr, n, _ptr(out, _dp), _ptr(lse, _dp))
+    out, lse = out[:n], lse[:n]
+    return (out, lse) if with_lse else out
+
+
+def euler_step(z, x0, t, t_next, t_eps=0.02) -> np.ndarray:
+    """One x0->velocity Euler update; [A] §Flow matching without a VAE."""
+    z = _f64(z).copy()
+    x0 = _f64(x0)
+    assert z.shape == x0.shape
+    _load().oracle_euler_step(_ptr(z, _dp), _ptr(x0, _dp), z.size, float(t), float(t_next),
+                              float(t_eps))
+    return z

@@ -1,0 +1,366 @@
+"""Pins for the fp64 oracle: values and properties fixed by the pages and by
+mathematics, independent of the oracle's own code.
+
+Each test names what it would catch.  Pages:
+  [A] "SenseNova-U1.5 (NEO-unify) architecture" (Mobius design note)
+  [B] "SenseNova-U1: Unifying Multimodal Understanding and Generation with
+      NEO-unify Architecture" (paper notes)
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------------------
+# Euler update: [A] §Flow matching without a VAE; [B] §2.2 and §2.7
+# --------------------------------------------------------------------------------------
+
+def test_euler_worked_example():
+    """[B] §2.2 numeric example: t=0.6, x=1, eps=0, sigma_R=1 gives z_t=0.6, v*=1.0.
+
+    A perfect x0 prediction (x0 = x) taken from z_t must move z by dt * v*; with
+    t_next = 1 it lands exactly on x.  Catches a wrong divisor (t instead of 1-t),
+    a wrong sign in (x0 - z) or a dropped dt."""
+    g = _golden("fm_worked_example.json")
+    z_t = g["t"] * g["x"] + (1 - g["t"]) * g["sigma_R"] * g["epsilon"]
+    assert z_t == pytest.approx(g["z_t"], abs=1e-15)
+    for t_next in (0.7, 0.8, 1.0):
+        z1 = oracle.euler_step([g["z_t"]], [g["x"]], g["t"], t_next)[0]
+        v = (z1 - g["z_t"]) / (t_next - g["t"])
+        assert v == pytest.approx(g["v_star"], abs=1e-12)
+    assert oracle.euler_step([g["z_t"]], [g["x"]], g["t"], 1.0)[0] == pytest.approx(g["x"], abs=1e-15)
+
+
+def test_euler_clamp_cases():
+    """max(1 - t, t_eps) divisor: the clamp branch and the plain branch at fixed values."""
+    for c in _golden("euler_clamp.json")["cases"]:
+        got = oracle.euler_step([c["z"]], [c["x0"]], c["t"], c["t_next"], c["t_eps"])[0]
+        assert got == pytest.approx(c["z_next"], abs=1e-12), c["why"]
+
+
+def test_euler_trajectory_stays_on_interpolant():
+    """Closed form: with x0 fixed to the clean x, Euler from z_0 = sigma*eps at t=0
+    reproduces z_t = t x + (1 - t) sigma eps at every grid point and ends at x.
+    Catches any error in the step that a single-point check could hide."""
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(1000)
+    eps = rng.standard_normal(1000)
+    sigma = 2.0
+    S = 20
+    z = sigma * eps
+    for k in range(S):
+        t, tn = k / S, (k + 1) / S
+        z = oracle.euler_step(z, x, t, tn)
+        np.testing.assert_allclose(z, tn * x + (1 - tn) * sigma * eps, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(z, x, atol=1e-12, rtol=0)
+
+
+# --------------------------------------------------------------------------------------
+# Split-half RMSNorm: [A] §Three rotary axes, last paragraph
+# --------------------------------------------------------------------------------------
+
+def test_norm_constant_halves_closed_form():
+    """x = c1 on [0:64), c2 on [64:128) gives w_t*c1/sqrt(c1^2+eps) and
+    w_hw*c2/sqrt(c2^2+eps).  Catches normalising over all 128 dims, swapping the
+    two weights, or forgetting eps."""
+    eps = 0.25
+    c1, c2 = 3.0, -0.5
+    x = np.concatenate([np.full(64, c1), np.full(64, c2)])[None]
+    w_t = np.linspace(0.5, 1.5, 64)
+    w_hw = np.linspace(2.0, -1.0, 64)
+    y = oracle.split_rmsnorm(x, w_t, w_hw, eps)[0]
+    np.testing.assert_allclose(y[:64], w_t * c1 / math.sqrt(c1 * c1 + eps), rtol=1e-14)
+    np.testing.assert_allclose(y[64:], w_hw * c2 / math.sqrt(c2 * c2 + eps), rtol=1e-14)
+
+
+def test_norm_unit_weight_rms():
+    """With unit weights each half's output RMS is sqrt(ms / (ms + eps))."""
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((50, 128)) * 0.01
+    eps = 1e-4
+    y = oracle.split_rmsnorm(x, np.ones(64), np.ones(64), eps)
+    for s in (slice(0, 64), slice(64, 128)):
+        ms = np.mean(x[:, s] ** 2, axis=1)
+        np.testing.assert_allclose(np.sqrt(np.mean(y[:, s] ** 2, axis=1)),
+                                   np.sqrt(ms / (ms + eps)), rtol=1e-12)
+
+
+def test_norm_halves_independent_and_scale_invariant():
+    """Changing one half leaves the other half's output unchanged; scaling a half by
+    alpha leaves its output unchanged when eps is negligible."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((8, 128))
+    w_t, w_hw = rng.uniform(0.5, 1.5, 64), rng.uniform(0.5, 1.5, 64)
+    y = oracle.split_rmsnorm(x, w_t, w_hw, 1e-6)
+    x2 = x.copy()
+    x2[:, 64:] *= 7.0
+    x2[:, 64:] += 1.0
+    y2 = oracle.split_rmsnorm(x2, w_t, w_hw, 1e-6)
+    np.testing.assert_array_equal(y[:, :64], y2[:, :64])
+    y0 = oracle.split_rmsnorm(x, w_t, w_hw, 0.0)
+    y3 = oracle.split_rmsnorm(x * 1000.0, w_t, w_hw, 0.0)
+    np.testing.assert_allclose(y3, y0, rtol=1e-12, atol=1e-14)
+
+
+# --------------------------------------------------------------------------------------
+# Three-axis rotary: [A] §Three rotary axes (table), §Vision tower (half-split backbone)
+# --------------------------------------------------------------------------------------
+
+def _one_hot(d):
+    x = np.zeros((1, 1, 128))
+    x[0, 0, d] = 1.0
+    return x
+
+
+def test_rope_one_hot_closed_form():
+    """Rotating the unit vector e_d gives cos(phi) at d and +-sin(phi) at its partner
+    d +- w/2, with phi = p * base^(-2i/w) for slice (start, width w, base, position
+    row) from the page's table.  Checks, per slice: the slice boundaries, which
+    position row drives it, its base, the frequency exponent, the half-split
+    pairing and the rotation's sign."""
+    table = _golden("rope_axes.json")["slices"]
+    theta = [s_["base"] for s_ in table if s_["axis"] == "temporal"][0]
+    theta_hw = [s_["base"] for s_ in table if s_["axis"] == "height"][0]
+    assert [s_["base"] for s_ in table if s_["axis"] == "width"][0] == theta_hw
+    pos = np.array([[37], [11], [5]], dtype=np.int32)  # temporal, height, width
+    for sl in table:
+        o, w, base = sl["start"], sl["stop"] - sl["start"], sl["base"]
+        p = float(pos[sl["position_row"], 0])
+        half = w // 2
+        for i in (0, 1, half // 2, half - 1):
+            phi = p * base ** (-2.0 * i / w)
+            # first element of the pair: (a, b) = (1, 0) -> (cos, sin)
+            y = oracle.rope3(_one_hot(o + i), pos, theta, theta_hw)[0, 0]
+            expect = np.zeros(128)
+            expect[o + i] = math.cos(phi)
+            expect[o + i + half] = math.sin(phi)
+            np.testing.assert_allclose(y, expect, atol=1e-13)
+            # second element of the pair: (a, b) = (0, 1) -> (-sin, cos)
+            y = oracle.rope3(_one_hot(o + i + half), pos, theta, theta_hw)[0, 0]
+            expect = np.zeros(128)
+            expect[o + i] = -math.sin(phi)
+            expect[o + i + half] = math.cos(phi)
+            np.testing.assert_allclose(y, expect, atol=1e-13)
+
+
+def test_rope_position_zero_is_identity():
+    """Text tokens sit at h = w = 0, so their spatial dims are left unrotated; at
+    p = 0 on every axis the whole row is unchanged."""
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((3, 2, 128))
+    pos = np.array([[0, 5, 9], [0, 0, 0], [0, 0, 0]], dtype=np.int32)
+    y = oracle.rope3(x, pos)
+    np.testing.assert_array_equal(y[0], x[0])
+    np.testing.assert_array_equal(y[1:, :, 64:], x[1:, :, 64:])
+    assert not np.allclose(y[1:, :, :64], x[1:, :, :64])
+
+
+def test_rope_pair_norms_preserved():
+    """Every rotated pair keeps its length (orthogonality; catches a sign slip)."""
+    rng = np.random.default_rng(5)
+    T, H = 6, 3
+    x = rng.standard_normal((T, H, 128))
+    pos = rng.integers(0, 3000, size=(3, T)).astype(np.int32)
+    y = oracle.rope3(x, pos)
+    for o, w in ((0, 64), (64, 32), (96, 32)):
+        h = w // 2
+        n_x = x[..., o:o + h] ** 2 + x[..., o + h:o + w] ** 2
+        n_y = y[..., o:o + h] ** 2 + y[..., o + h:o + w] ** 2
+        np.testing.assert_allclose(n_y, n_x, rtol=1e-12)
+
+
+def test_rope_composition():
+    """R(a) R(b) = R(a + b) on every axis."""
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((4, 2, 128))
+    a = rng.integers(0, 500, size=(3, 4)).astype(np.int32)
+    b = rng.integers(0, 500, size=(3, 4)).astype(np.int32)
+    np.testing.assert_allclose(oracle.rope3(oracle.rope3(x, a), b), oracle.rope3(x, a + b),
+                               atol=1e-11)
+
+
+def test_rope_relative_position():
+    """Per axis slice, <R(p) q, R(p') k> depends only on p - p': shifting one axis of
+    both positions by a constant leaves every slice's score unchanged."""
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((1, 1, 128))
+    k = rng.standard_normal((1, 1, 128))
+    pq = np.array([[700], [13], [40]], dtype=np.int32)
+    pk = np.array([[512], [3], [61]], dtype=np.int32)
+
+    def slice_scores(pq_, pk_):
+        a, b = oracle.rope3(q, pq_)[0, 0], oracle.rope3(k, pk_)[0, 0]
+        return [float(a[s] @ b[s]) for s in (slice(0, 64), slice(64, 96), slice(96, 128))]
+
+    base = slice_scores(pq, pk)
+    for axis, shift in ((0, 1234), (1, 50), (2, 7)):
+        dq, dk = pq.copy(), pk.copy()
+        dq[axis] += shift
+        dk[axis] += shift
+        np.testing.assert_allclose(slice_scores(dq, dk), base, atol=1e-10)
+    # and a change of the difference on one axis changes exactly that slice
+    dq = pq.copy()
+    dq[1] += 1
+    moved = slice_scores(dq, pk)
+    assert moved[0] == pytest.approx(base[0], abs=1e-12)
+    assert moved[2] == pytest.approx(base[2], abs=1e-12)
+    assert abs(moved[1] - base[1]) > 1e-6
+
+
+def test_norm_rope_order():
+    """norm_rope is the norm followed by the rotary (the rotary preserves pair
+    lengths, so the per-half RMS after both steps still equals the norm's)."""
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((5, 2, 128))
+    pos = rng.integers(0, 100, size=(3, 5)).astype(np.int32)
+    w1, w2 = np.ones(64), np.ones(64)
+    y = oracle.norm_rope(x, w1, w2, pos, eps=0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y[..., :64] ** 2, -1)), 1.0, rtol=1e-12)
+    np.testing.assert_allclose(np.sqrt(np.mean(y[..., 64:] ** 2, -1)), 1.0, rtol=1e-12)
+    np.testing.assert_allclose(y, oracle.rope3(oracle.split_rmsnorm(x, w1, w2, 0.0), pos),
+                               atol=1e-14)
+
+
+# --------------------------------------------------------------------------------------
+# Generation-pass attention: [A] §Mixture of Transformers, §GQA fusion does not apply
+# --------------------------------------------------------------------------------------
+
+def _attn_inputs(rng, n_img, n_pre, Hq, Hkv, D=128):
+    Tq, Tp = sum(n_img), sum(n_pre)
+    return dict(q=rng.standard_normal((Tq, Hq, D)), k_img=rng.standard_normal((Tq, Hkv, D)),
+                v_img=rng.standard_normal((Tq, Hkv, D)), k_pre=rng.standard_normal((Tp, Hkv, D)),
+                v_pre=rng.standard_normal((Tp, Hkv, D)),
+                cu_q=np.concatenate([[0], np.cumsum(n_img)]).astype(np.int32),
+                cu_p=np.concatenate([[0], np.cumsum(n_pre)]).astype(np.int32))
+
+
+def test_attn_two_key_closed_form():
+    """One prefix key with score ln 3 (after the 1/sqrt(128) scale) and one image key
+    with score 0: weights 3/4 and 1/4, so O = 0.75*v1 + 0.25*v2 and lse = ln 4.
+    Catches a missing or wrong softmax scale and a wrong lse."""
+    D = 128
+    q = np.zeros((1, 1, D))
+    q[0, 0, 0] = math.sqrt(D)
+    k_pre = np.zeros((1, 1, D))
+    k_pre[0, 0, 0] = math.log(3.0)
+    k_img = np.zeros((1, 1, D))
+    v_pre = np.full((1, 1, D), 2.0)
+    v_img = np.full((1, 1, D), -6.0)
+    out, lse = oracle.gen_attn(q, k_img, v_img, k_pre, v_pre, [0, 1], [0, 1], with_lse=True)
+    np.testing.assert_allclose(out[0, 0], 0.75 * 2.0 + 0.25 * -6.0, atol=1e-14)
+    assert lse[0, 0] == pytest.approx(math.log(4.0), abs=1e-14)
+
+
+def test_attn_gqa_head_map():
+    """V of KV head g is the constant g + 1, so query head h must return
+    h // (Hq/Hkv) + 1.  Catches h % Hkv or any other head map."""
+    rng = np.random.default_rng(9)
+    Hq, Hkv = 8, 2
+    a = _attn_inputs(rng, [5], [3], Hq, Hkv)
+    for g in range(Hkv):
+        a["v_img"][:, g, :] = g + 1
+        a["v_pre"][:, g, :] = g + 1
+    out = oracle.gen_attn(**a)
+    for h in range(Hq):
+        np.testing.assert_allclose(out[:, h, :], h // (Hq // Hkv) + 1, atol=1e-13)
+
+
+def test_attn_key_set_per_sample():
+    """Sample b sees exactly its own prefix rows and its own image rows: with q = 0
+    every key weighs the same, so O = (P_b*a_b + N_b*c_b)/(P_b + N_b) for prefix
+    value a_b and image value c_b.  Catches dropping a segment, off-by-one ranges
+    and leakage across samples."""
+    rng = np.random.default_rng(10)
+    n_img, n_pre = [3, 5, 2], [4, 0, 7]
+    a = _attn_inputs(rng, n_img, n_pre, 2, 1)
+    a["q"][:] = 0.0
+    for b in range(3):
+        a["v_pre"][a["cu_p"][b]:a["cu_p"][b + 1]] = 10.0 * b + 1
+        a["v_img"][a["cu_q"][b]:a["cu_q"][b + 1]] = -(10.0 * b + 3)
+    out = oracle.gen_attn(**a)
+    for b in range(3):
+        P, N = n_pre[b], n_img[b]
+        expect = (P * (10.0 * b + 1) - N * (10.0 * b + 3)) / (P + N)
+        np.testing.assert_allclose(out[a["cu_q"][b]:a["cu_q"][b + 1]], expect, atol=1e-12)
+
+
+def test_attn_brute_force_tiny():
+    """Brute force on a tiny case with numpy: scores as a matrix product, softmax,
+    weighted sum over the concatenated key set."""
+    rng = np.random.default_rng(11)
+    a = _attn_inputs(rng, [6], [5], 4, 2)
+    out, lse = oracle.gen_attn(**a, with_lse=True)
+    for h in range(4):
+        g = h // 2
+        K = np.concatenate([a["k_pre"][:, g], a["k_img"][:, g]])
+        V = np.concatenate([a["v_pre"][:, g], a["v_img"][:, g]])
+        S = a["q"][:, h] @ K.T / math.sqrt(128)
+        P = np.exp(S - S.max(1, keepdims=True))
+        np.testing.assert_allclose(out[:, h], (P / P.sum(1, keepdims=True)) @ V, atol=1e-13)
+        np.testing.assert_allclose(lse[:, h], np.log(np.exp(S).sum(1)), atol=1e-12)
+
+
+def test_attn_single_key_and_constant_v():
+    """A single key returns its value; a constant V returns that constant."""
+    rng = np.random.default_rng(12)
+    a = _attn_inputs(rng, [1], [0], 2, 1)
+    np.testing.assert_allclose(oracle.gen_attn(**a)[0, 0], a["v_img"][0, 0], atol=1e-15)
+    b = _attn_inputs(rng, [4], [3], 2, 1)
+    b["v_img"][:] = 0.3
+    b["v_pre"][:] = 0.3
+    np.testing.assert_allclose(oracle.gen_attn(**b), 0.3, atol=1e-14)
+
+
+def test_attn_invariants():
+    """GQA equals MHA with repeated KV heads; a ragged batch equals separate calls;
+    permuting image tokens permutes the outputs; the order of prefix keys is
+    irrelevant."""
+    rng = np.random.default_rng(13)
+    Hq, Hkv = 6, 2
+    a = _attn_inputs(rng, [7, 3], [4, 9], Hq, Hkv)
+    out = oracle.gen_attn(**a)
+    rep = {k_: (np.repeat(v_, Hq // Hkv, axis=1) if k_ in ("k_img", "v_img", "k_pre", "v_pre")
+                else v_) for k_, v_ in a.items()}
+    np.testing.assert_allclose(oracle.gen_attn(**rep), out, atol=1e-13)
+    for b in range(2):
+        qs = slice(a["cu_q"][b], a["cu_q"][b + 1])
+        ps = slice(a["cu_p"][b], a["cu_p"][b + 1])
+        nq, npf = qs.stop - qs.start, ps.stop - ps.start
+        single = oracle.gen_attn(a["q"][qs], a["k_img"][qs], a["v_img"][qs], a["k_pre"][ps],
+                                 a["v_pre"][ps], [0, nq], [0, npf])
+        np.testing.assert_allclose(single, out[qs], atol=1e-13)
+    perm = rng.permutation(7)
+    p = dict(a)
+    for k_ in ("q", "k_img", "v_img"):
+        p[k_] = a[k_].copy()
+        p[k_][:7] = a[k_][:7][perm]
+    np.testing.assert_allclose(oracle.gen_attn(**p)[:7], out[:7][perm], atol=1e-13)
+    one = _attn_inputs(rng, [4], [5], 2, 1)
+    ref = oracle.gen_attn(**one)
+    order = rng.permutation(5)
+    swapped = dict(one)
+    swapped["k_pre"], swapped["v_pre"] = one["k_pre"][order], one["v_pre"][order]
+    np.testing.assert_allclose(oracle.gen_attn(**swapped), ref, atol=1e-13)
+
+
+def test_attn_sampled_rows_match_full():
+    """Evaluating a sampled set of query rows returns the same values as the full call."""
+    rng = np.random.default_rng(14)
+    a = _attn_inputs(rng, [5, 6], [3, 2], 4, 1)
+    full, lse = oracle.gen_attn(**a, with_lse=True)
+    rows = np.array([10, 0, 7, 5])
+    part, lse_p = oracle.gen_attn(**a, tokens=rows, with_lse=True)
+    np.testing.assert_array_equal(part, full[rows])
+    np.testing.assert_array_equal(lse_p, lse[rows])
