@@ -1,0 +1,225 @@
+"""Benchmark of the generation-pass attention block on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input:
+split-half QK-RMSNorm + three-axis rotary on the image queries and keys, the
+image queries' attention over [512-token frozen prefix ; 4096 image tokens],
+and one x0 -> velocity Euler step on the 3x2048x2048 pixel tensor.  Inputs are
+resident in HBM before the timed region; a few input sets are rotated so the
+bandwidth-bound kernels are not served from the 256 MB Infinity Cache.
+
+Prints one JSON line.  value = image tokens per second per step (4096 / step
+time).  roofline = the attention kernel's achieved bf16 MFMA TFLOP/s (algorithmic
+4*Hq*D*N*(P+N) flops over its average event-timed duration) against the 2.5
+PFLOP/s dense peak.  cpu_baseline = the fp64 oracle on the host cores, on a
+bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "gen-pass attention TFLOP/s + image-tokens/s per FM step at 4096 tokens (1 GPU)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="large", choices=["large", "mid", "small", "editing"])
+    ap.add_argument("--sets", type=int, default=4, help="rotated input sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=256,
+                    help="query tokens in the oracle's attention sample")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM bytes per launch measured with rocprofv3 counters, if present")
+    return ap.parse_args()
+
+
+def algorithmic(w):
+    D = 128
+    flops = 4.0 * w.Hq * D * sum(n * (p + n) for n, p in zip(w.n_img, w.n_prefix))
+    pro_bytes = w.Tq * ((w.Hq + w.Hkv) * D * 2 * 2 + 3 * 4)   # bf16 read + write, positions
+    npx = int(np.prod(w.pixel_shape))
+    euler_bytes = npx * 12                                     # fp32 z, x0 read; z written
+    attn_bytes = (w.Tq * (w.Hq * 2 + w.Hkv * 2) + w.Tp * w.Hkv * 2) * D * 2
+    return flops, pro_bytes, euler_bytes, attn_bytes
+
+
+def cpu_baseline(w, kp, vp, n_tokens):
+    import oracle
+    t0 = time.perf_counter()
+    qr, kr = oracle.qknorm_rope3(w.q, w.k, w.wq_t, w.wq_hw, w.wk_t, w.wk_hw, w.pos_img,
+                                 w.rope_theta, w.rope_theta_hw, w.eps)
+    t_pro = time.perf_counter() - t0
+    rows = np.linspace(0, w.Tq - 1, n_tokens).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.gen_attn(qr, kr, w.v, kp, vp, w.cu_q, w.cu_p, tokens=rows)
+    t_attn = (time.perf_counter() - t0) * (w.Tq / n_tokens)
+    z0 = np.float32(w.sigma_R) * w.eps_pixels
+    t0 = time.perf_counter()
+    oracle.euler_step(z0, w.x_hat, w.t_grid[0], w.t_grid[1], w.t_eps)
+    t_eul = time.perf_counter() - t0
+    t_step = t_pro + t_attn + t_eul
+    return {
+        "value": w.Tq / t_step, "unit": "image-tokens/s", "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"fp64 oracle: norm+rotary on all {w.Tq} tokens and the Euler step on all "
+                   f"{int(np.prod(w.pixel_shape))} pixels; attention on {n_tokens} of {w.Tq} "
+                   f"query tokens (all {w.Hq} heads, all keys), time scaled by "
+                   f"{w.Tq / n_tokens:g}"),
+        "seconds": {"prologue": t_pro, "attention_scaled": t_attn, "euler": t_eul},
+    }
+
+
+def main():
+    a = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the block shards by KV head or by CFG branch with no exchange inside it). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import pixel_space_flow_amd as neo
+    import workloads as W
+    from tests import harness as H
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    neo.lib()
+
+    w = W.make(a.workload)
+    if w.prefix_kind == "direct":
+        kp, vp = w.k_prefix, w.v_prefix
+    else:
+        kp, vp = H.frozen_prefix(w)
+    flops, pro_bytes, euler_bytes, attn_bytes = algorithmic(w)
+
+    # input sets resident in HBM; each set perturbs the seeded inputs so buffers differ
+    sets = []
+    z0 = (np.float32(w.sigma_R) * w.eps_pixels).astype(np.float32)
+    base = dict(q=H.dev(w.q, "bf16"), k=H.dev(w.k, "bf16"), v=H.dev(w.v, "bf16"),
+                z=H.dev_f32(z0), x=H.dev_f32(w.x_hat))
+    for s in range(a.sets):
+        sets.append({
+            "q": base["q"].roll(s, 0).contiguous(), "k": base["k"].roll(s, 0).contiguous(),
+            "v": base["v"].roll(s, 0).contiguous(), "z": base["z"].roll(s).contiguous(),
+            "x": base["x"].roll(s).contiguous(),
+            "qo": torch.empty_like(base["q"]), "ko": torch.empty_like(base["k"]),
+            "out": torch.empty_like(base["q"]),
+        })
+    del base
+    shared = dict(kp=H.dev(kp, "bf16"), vp=H.dev(vp, "bf16"), cu_q=H.dev_i32(w.cu_q),
+                  cu_p=H.dev_i32(w.cu_p), wq_t=H.dev_f32(w.wq_t), wq_hw=H.dev_f32(w.wq_hw),
+                  wk_t=H.dev_f32(w.wk_t), wk_hw=H.dev_f32(w.wk_hw), pos=H.dev_i32(w.pos_img))
+    max_q, max_p = max(w.n_img), max(w.n_prefix)
+    t, tn = w.t_grid[0], w.t_grid[1]
+
+    def step(i, ev=None):
+        s = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record()
+        neo.qknorm_rope3(s["q"], s["k"], shared["wq_t"], shared["wq_hw"], shared["wk_t"],
+                         shared["wk_hw"], shared["pos"], w.rope_theta, w.rope_theta_hw, w.eps,
+                         q_out=s["qo"], k_out=s["ko"])
+        if ev is not None:
+            ev[1].record()
+        neo.gen_attn_fwd(s["qo"], s["ko"], s["v"], shared["kp"], shared["vp"], shared["cu_q"],
+                         shared["cu_p"], max_q, max_p, out=s["out"])
+        if ev is not None:
+            ev[2].record()
+        neo.fm_euler_step(s["z"], s["x"], t, tn, w.t_eps)
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({a.warmup} steps)", file=sys.stderr, flush=True)
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / a.steps
+    pro_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    att_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    eul_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
+    print(f"[bench] timed {a.steps} steps: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    attn_s = float(att_ms.mean()) * 1e-3
+    achieved = flops / attn_s / 1e12
+    traffic = None
+    if os.path.exists(a.traffic_json):
+        with open(a.traffic_json) as f:
+            tj = json.load(f)
+        traffic = tj.get("gen_attn_bf16_kernel", {}).get(a.workload)
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic}
+    pro_gbs = pro_bytes / (float(pro_ms.mean()) * 1e-3) / 1e9
+    eul_gbs = euler_bytes / (float(eul_ms.mean()) * 1e-3) / 1e9
+    gpu_step_s = float((pro_ms + att_ms + eul_ms).mean()) * 1e-3
+    roof_step_s = flops / (PEAK_BF16_TFLOPS * 1e12) + (pro_bytes + euler_bytes) / (PEAK_HBM_GBS * 1e9)
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, kp, vp, a.cpu_tokens)
+
+    ntok = w.Tq
+    result = {
+        "metric": METRIC,
+        "value": ntok / (ms_step * 1e-3),
+        "unit": "image-tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{a.workload}: {w.B} sample(s), {ntok} image tokens "
+                         f"({w.pixel_shape[2]}x{w.pixel_shape[3]} px), prefix {w.n_prefix}, "
+                         f"Hq={w.Hq}, Hkv={w.Hkv}, head_dim=128; one norm+rotary, one "
+                         f"attention and one Euler step per step"),
+            "batch": w.B, "image_tokens": ntok, "prefix_tokens": w.Tp,
+            "pixels": list(w.pixel_shape), "input_sets": a.sets,
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "attention_tflops": achieved,
+        "kernels_us": {"qknorm_rope3": float(pro_ms.mean()) * 1e3,
+                       "gen_attn": float(att_ms.mean()) * 1e3,
+                       "fm_euler_step": float(eul_ms.mean()) * 1e3},
+        "hbm_gbs": {"qknorm_rope3": pro_gbs, "fm_euler_step": eul_gbs},
+        "hbm_frac": {"qknorm_rope3": pro_gbs / PEAK_HBM_GBS, "fm_euler_step": eul_gbs / PEAK_HBM_GBS},
+        "step_roofline": {"tokens_per_s_at_roofline": ntok / roof_step_s,
+                          "frac": (ntok / gpu_step_s) / (ntok / roof_step_s)},
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,169 @@
+/*
+ * neo.h -- C ABI of the NEO-unify generation-pass attention block for MI355X
+ * (gfx950).
+ *
+ * Pages cited:
+ *   [A] "SenseNova-U1.5 (NEO-unify) architecture" (Mobius design note)
+ *   [B] "SenseNova-U1: Unifying Multimodal Understanding and Generation with
+ *        NEO-unify Architecture" (paper notes)
+ *
+ * The generation pass runs once per flow-matching step: the noisy image tokens,
+ * already projected with the generation-branch weights, get split-half
+ * QK-RMSNorm and three-axis rotary ([A] §Three rotary axes), then the image
+ * queries attend, unmasked and without writing the cache, over the frozen
+ * understanding-branch K/V prefix followed by the image block's own K/V
+ * ([A] §Mixture of Transformers; §GQA fusion does not apply).  The sampler
+ * turns the predicted clean image into a velocity and takes one Euler step
+ * ([A] §Flow matching without a VAE).
+ *
+ * Conventions for every entry point:
+ *   - Plain C: no C++ types, no HIP headers are needed to include this file.
+ *   - Device pointers are HIP device (or managed) memory on the current
+ *     device; the caller owns every buffer.  The library allocates nothing,
+ *     keeps no state besides a thread-local error message, and never
+ *     synchronises: work is enqueued on `hip_stream` (a hipStream_t; NULL is
+ *     the null stream) and outputs are valid once that stream is synchronised.
+ *   - Layouts are token-major and contiguous: a [T, H, 128] tensor has row
+ *     (t, h) at element offset (t*H + h)*128 ([B] §4.4 KV cache reuse: the
+ *     cache is kept as [B, S, H, D], flattened here over the ragged batch).
+ *   - Arguments are validated on the host before any HIP call; a failed check
+ *     returns a non-zero neo_status and launches nothing.  neo_last_error()
+ *     then describes the failure for the calling thread.
+ *   - Only the generation pass is served.  Anything outside it (a mask, a
+ *     cache update, another head size) is rejected with NEO_ERR_UNSUPPORTED,
+ *     as the upstream code refuses mixed understanding/generation calls
+ *     ([A] §Mixture of Transformers).
+ */
+#ifndef NEO_H
+#define NEO_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NEO_OK = 0,
+    NEO_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    NEO_ERR_SHAPE = 2,       /* a size or count is out of range               */
+    NEO_ERR_VALUE = 3,       /* a scalar is non-finite or out of its domain   */
+    NEO_ERR_UNSUPPORTED = 4, /* outside the generation-pass contract          */
+    NEO_ERR_HIP = 5          /* the HIP runtime reported an error at launch   */
+} neo_status;
+
+typedef enum {
+    NEO_F32 = 0,  /* IEEE binary32                                            */
+    NEO_BF16 = 1  /* bfloat16 (upper half of binary32), round-to-nearest-even */
+} neo_dtype;
+
+#define NEO_HEAD_DIM 128
+
+/*
+ * neo_qknorm_rope3 -- split-half QK-RMSNorm then three-axis rotary on the
+ * generation block's queries and keys.
+ *
+ * Defined by [A] §Three rotary axes: each 128-dim head row is normalised as two
+ * independent 64-dim halves, y = x / sqrt(mean(x^2) + eps) * w, with w =
+ * q_norm_w (k_norm_w) on dims [0:64) and q_norm_hw_w (k_norm_hw_w) on dims
+ * [64:128).  The row is then rotated per slice:
+ *     dims [0:64)   by pos_thw[0][t] with base rope_theta     (temporal),
+ *     dims [64:96)  by pos_thw[1][t] with base rope_theta_hw  (height),
+ *     dims [96:128) by pos_thw[2][t] with base rope_theta_hw  (width),
+ * pairing element o+i with o+i+w/2 inside a slice of width w (half-split, as
+ * [A] §Vision tower says of the language backbone) at angle
+ * pos * base^(-2i/w).  All image tokens of one image carry the same temporal
+ * index, the text length ([A] §Three rotary axes).
+ *
+ *   q_in   [T, Hq, 128]  dtype; device; read.
+ *   k_in   [T, Hkv, 128] dtype; device; read.
+ *   q_out  [T, Hq, 128]  dtype; device; written.  May equal q_in (in place).
+ *   k_out  [T, Hkv, 128] dtype; device; written.  May equal k_in (in place).
+ *          Partial overlap of an input and an output is not allowed.
+ *   T      tokens, >= 0 (0 is a no-op).  Hq, Hkv >= 1.  head_dim == 128.
+ *   q_norm_w, q_norm_hw_w, k_norm_w, k_norm_hw_w   [64] fp32, device.
+ *   pos_thw  [3, T] int32, device: temporal, height, width rows.
+ *   rope_theta, rope_theta_hw  > 0 and finite (the pages: 5e6 and 1e4).
+ *   eps    >= 0 and finite (1e-6 in the workloads).
+ *   Arithmetic is fp32; a bf16 output is rounded once, after the rotary.
+ */
+neo_status neo_qknorm_rope3(const void *q_in, const void *k_in, void *q_out, void *k_out,
+                            int64_t T, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                            const float *q_norm_w, const float *q_norm_hw_w,
+                            const float *k_norm_w, const float *k_norm_hw_w,
+                            const int32_t *pos_thw, float rope_theta, float rope_theta_hw,
+                            float eps, neo_dtype dtype, void *hip_stream);
+
+/*
+ * neo_gen_attn_fwd -- generation-pass attention of the image queries over
+ * [frozen prefix ; image block], no mask, no cache write.
+ *
+ * Defined by [A] §Mixture of Transformers (the generation pass reads the keys
+ * and values the understanding pass wrote, with update_cache=False) and
+ * §GQA fusion does not apply (the generation pass is unmasked).  For sample b,
+ * query row i in [cu_seqlens_q[b], cu_seqlens_q[b+1]) and query head h, with
+ * g = h / (Hq / Hkv):
+ *     keys    = k_prefix rows [cu_seqlens_prefix[b], cu_seqlens_prefix[b+1])
+ *               followed by k_img rows [cu_seqlens_q[b], cu_seqlens_q[b+1]),
+ *     out[i,h] = sum_j softmax_j(softmax_scale * <q[i,h], key_j[g]>) value_j[g],
+ *     lse[h,i] = log sum_j exp(softmax_scale * <q[i,h], key_j[g]>).
+ *
+ *   q        [Tq, Hq, 128]  dtype, device: queries after norm and rotary.
+ *   k_img    [Tq, Hkv, 128] dtype, device: the image block's keys (rotated).
+ *   v_img    [Tq, Hkv, 128] dtype, device.
+ *   k_prefix [Tp, Hkv, 128] dtype, device: the frozen cache, already rotated.
+ *   v_prefix [Tp, Hkv, 128] dtype, device.  With Tp == 0 both may be NULL.
+ *   cu_seqlens_q      [B+1] int32, device: 0 = c[0] <= c[1] <= ... = Tq.
+ *   cu_seqlens_prefix [B+1] int32, device: 0 = c[0] <= ... = Tp.
+ *   B >= 1.  Hq, Hkv >= 1 with Hq % Hkv == 0.  head_dim == 128.
+ *   total_q (Tq), total_prefix (Tp) >= 0: row counts of the tensors above, on
+ *     the host.  The kernels clamp every cu_seqlens entry into [0, Tq] and
+ *     [0, Tp], so malformed offsets give wrong numbers, never a stray access.
+ *   max_seqlen_q, max_seqlen_prefix: host-side upper bounds of the per-sample
+ *     lengths (no device-to-host copy is made); they size the launch grid and
+ *     must not be below the true maxima (a precondition, as in varlen flash
+ *     attention: rows and keys beyond the bound are not computed).
+ *   softmax_scale: <= 0 selects 1/sqrt(head_dim); otherwise finite.
+ *   out      [Tq, Hq, 128] dtype, device: written.  Must not overlap inputs.
+ *   lse      [Hq, Tq] fp32, device, natural log, or NULL to skip.
+ *   A sample with no keys (P_b + N_b == 0) has no queries either, so no
+ *   output row is ever left undefined.
+ */
+neo_status neo_gen_attn_fwd(const void *q, const void *k_img, const void *v_img,
+                            const void *k_prefix, const void *v_prefix,
+                            const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_prefix,
+                            int32_t B, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                            int64_t total_q, int64_t total_prefix,
+                            int32_t max_seqlen_q, int32_t max_seqlen_prefix,
+                            float softmax_scale, void *out, float *lse, neo_dtype dtype,
+                            void *hip_stream);
+
+/*
+ * neo_fm_euler_step -- x0-prediction to velocity and one Euler step of the
+ * pixel-space rectified flow, in place:
+ *     v = (x0_pred - z) / max(1 - t, t_eps);   z <- z + (t_next - t) * v
+ * ([A] §Flow matching without a VAE and §Runtime / metadata status; [B] §2.7).
+ * patchify is a pure permutation, so the update is elementwise on any layout.
+ *
+ *   z        [n] fp32, device: read and written.
+ *   x0_pred  [n] fp32, device: read.  May not partially overlap z.
+ *   n >= 0 (0 is a no-op).
+ *   t, t_next finite with t <= t_next; t_eps > 0 and finite (0.02 is the
+ *   value real inference uses, [A] §Dead or misleading upstream details).
+ *   Arithmetic is fp32: z + c*(x0_pred - z) with c = (t_next - t)/max(1-t, t_eps)
+ *   formed once in double on the host.
+ */
+neo_status neo_fm_euler_step(float *z, const float *x0_pred, int64_t n, float t, float t_next,
+                             float t_eps, void *hip_stream);
+
+/* Static English text for a status code; never NULL. */
+const char *neo_status_string(neo_status s);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char *neo_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NEO_H */

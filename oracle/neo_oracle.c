@@ -52,6 +52,7 @@ int oracle_num_threads(void)
 void oracle_split_rmsnorm(const double *x, double *y, int64_t rows,
                           const double *w_t, const double *w_hw, double eps)
 {
+#pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         const double *xr = x + r * HEAD_DIM;
         double *yr = y + r * HEAD_DIM;
@@ -84,6 +85,7 @@ void oracle_rope3(double *y, int64_t T, int64_t H, const int32_t *pos,
 {
     const int offset[3] = {0, 64, 96};
     const int width[3] = {64, 32, 32};
+#pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; ++t) {
         for (int64_t h = 0; h < H; ++h) {
             double *row = y + (t * H + h) * HEAD_DIM;
@@ -198,6 +200,7 @@ void oracle_euler_step(double *z, const double *x0, int64_t n,
                        double t, double t_next, double t_eps)
 {
     double denom = fmax(1.0 - t, t_eps);
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
         double v = (x0[i] - z[i]) / denom;
         z[i] = z[i] + (t_next - t) * v;

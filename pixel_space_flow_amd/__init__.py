@@ -1,0 +1,181 @@
+"""Python binding of libneo, the MI355X generation-pass attention block.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+declared in include/neo.h.  torch supplies device memory and the current stream.
+There is no fallback: if libneo.so is missing or fails to load, every call
+raises.
+
+Pages cited:
+  [A] "SenseNova-U1.5 (NEO-unify) architecture" (Mobius design note)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["qknorm_rope3", "gen_attn_fwd", "fm_euler_step", "NeoError", "lib", "LIB_PATH",
+           "EXPORTED_SYMBOLS", "NEO_OK", "NEO_ERR_NULL", "NEO_ERR_SHAPE", "NEO_ERR_VALUE",
+           "NEO_ERR_UNSUPPORTED", "NEO_ERR_HIP", "NEO_F32", "NEO_BF16"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libneo.so")
+
+NEO_OK, NEO_ERR_NULL, NEO_ERR_SHAPE, NEO_ERR_VALUE, NEO_ERR_UNSUPPORTED, NEO_ERR_HIP = range(6)
+NEO_F32, NEO_BF16 = 0, 1
+
+EXPORTED_SYMBOLS = ("neo_qknorm_rope3", "neo_gen_attn_fwd", "neo_fm_euler_step",
+                    "neo_status_string", "neo_last_error")
+
+_vp = ctypes.c_void_p
+_i32, _i64, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+
+
+class NeoError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn} failed with status {status}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libneo.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m pixel_space_flow_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.neo_qknorm_rope3.restype = ctypes.c_int
+        L.neo_qknorm_rope3.argtypes = [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp,
+                                       _vp, _vp, _f32, _f32, _f32, ctypes.c_int, _vp]
+        L.neo_gen_attn_fwd.restype = ctypes.c_int
+        L.neo_gen_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                       _i64, _i64, _i32, _i32, _f32, _vp, _vp, ctypes.c_int, _vp]
+        L.neo_fm_euler_step.restype = ctypes.c_int
+        L.neo_fm_euler_step.argtypes = [_vp, _vp, _i64, _f32, _f32, _f32, _vp]
+        L.neo_status_string.restype = ctypes.c_char_p
+        L.neo_status_string.argtypes = [ctypes.c_int]
+        L.neo_last_error.restype = ctypes.c_char_p
+        L.neo_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != NEO_OK:
+        detail = lib().neo_last_error().decode(errors="replace")
+        raise NeoError(fn, status, detail)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return NEO_BF16
+    if t.dtype == torch.float32:
+        return NEO_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _dev(t, name, dtype=None, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def qknorm_rope3(q, k, q_norm_w, q_norm_hw_w, k_norm_w, k_norm_hw_w, pos_thw,
+                 rope_theta=5.0e6, rope_theta_hw=1.0e4, eps=1e-6, q_out=None, k_out=None):
+    """Split-half QK-RMSNorm + three-axis rotary ([A] §Three rotary axes).
+
+    q [T, Hq, 128], k [T, Hkv, 128] (bf16 or fp32), norm weights [64] fp32,
+    pos_thw [3, T] int32.  Writes q_out/k_out (new tensors unless given; pass
+    q_out=q, k_out=k for in place) and returns them.
+    """
+    torch = _torch()
+    _dev(q, "q")
+    T, Hq, D = q.shape
+    _dev(k, "k", q.dtype)
+    Hkv = k.shape[1]
+    if k.shape[0] != T or k.shape[2] != D:
+        raise ValueError("k must be [T, Hkv, 128] with q's T")
+    for nm, w in (("q_norm_w", q_norm_w), ("q_norm_hw_w", q_norm_hw_w), ("k_norm_w", k_norm_w),
+                  ("k_norm_hw_w", k_norm_hw_w)):
+        _dev(w, nm, torch.float32, (64,))
+    _dev(pos_thw, "pos_thw", torch.int32, (3, T))
+    q_out = torch.empty_like(q) if q_out is None else _dev(q_out, "q_out", q.dtype, q.shape)
+    k_out = torch.empty_like(k) if k_out is None else _dev(k_out, "k_out", k.dtype, k.shape)
+    st = lib().neo_qknorm_rope3(q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), T,
+                                Hq, Hkv, D, q_norm_w.data_ptr(), q_norm_hw_w.data_ptr(),
+                                k_norm_w.data_ptr(), k_norm_hw_w.data_ptr(), pos_thw.data_ptr(),
+                                rope_theta, rope_theta_hw, eps, _dtype_code(q), _stream(q))
+    _check("neo_qknorm_rope3", st)
+    return q_out, k_out
+
+
+def gen_attn_fwd(q, k_img, v_img, k_prefix, v_prefix, cu_seqlens_q, cu_seqlens_prefix,
+                 max_seqlen_q, max_seqlen_prefix, softmax_scale=0.0, out=None,
+                 return_lse=False):
+    """Generation-pass attention over [frozen prefix ; image block] ([A] §Mixture of
+    Transformers; §GQA fusion does not apply).
+
+    q [Tq, Hq, 128]; k_img/v_img [Tq, Hkv, 128]; k_prefix/v_prefix [Tp, Hkv, 128]
+    (Tp may be 0); cu_seqlens_* int32 [B+1] on the device; max_seqlen_* host ints.
+    Returns out [Tq, Hq, 128] (and lse [Hq, Tq] fp32 if return_lse).
+    """
+    torch = _torch()
+    _dev(q, "q")
+    Tq, Hq, D = q.shape
+    _dev(k_img, "k_img", q.dtype)
+    _dev(v_img, "v_img", q.dtype, k_img.shape)
+    Hkv = k_img.shape[1]
+    _dev(k_prefix, "k_prefix", q.dtype)
+    _dev(v_prefix, "v_prefix", q.dtype, k_prefix.shape)
+    if k_prefix.dim() != 3 or (k_prefix.shape[0] > 0 and tuple(k_prefix.shape[1:]) != (Hkv, D)):
+        raise ValueError("k_prefix must be [Tp, Hkv, 128]")
+    _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    _dev(cu_seqlens_prefix, "cu_seqlens_prefix", torch.int32, cu_seqlens_q.shape)
+    B = cu_seqlens_q.shape[0] - 1
+    Tp = k_prefix.shape[0]
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype, q.shape)
+    lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device) if return_lse else None
+    pre_k = k_prefix.data_ptr() if Tp > 0 else None
+    pre_v = v_prefix.data_ptr() if Tp > 0 else None
+    st = lib().neo_gen_attn_fwd(q.data_ptr(), k_img.data_ptr(), v_img.data_ptr(), pre_k, pre_v,
+                                cu_seqlens_q.data_ptr(), cu_seqlens_prefix.data_ptr(), B, Hq, Hkv,
+                                D, Tq, Tp, int(max_seqlen_q), int(max_seqlen_prefix),
+                                float(softmax_scale), out.data_ptr(),
+                                lse.data_ptr() if lse is not None else None, _dtype_code(q),
+                                _stream(q))
+    _check("neo_gen_attn_fwd", st)
+    return (out, lse) if return_lse else out
+
+
+def fm_euler_step(z, x0_pred, t, t_next, t_eps=0.02):
+    """In place: z <- z + (t_next - t) * (x0_pred - z) / max(1 - t, t_eps)
+    ([A] §Flow matching without a VAE).  z and x0_pred are fp32 device tensors."""
+    torch = _torch()
+    _dev(z, "z", torch.float32)
+    _dev(x0_pred, "x0_pred", torch.float32, z.shape)
+    st = lib().neo_fm_euler_step(z.data_ptr(), x0_pred.data_ptr(), z.numel(), float(t),
+                                 float(t_next), float(t_eps), _stream(z))
+    _check("neo_fm_euler_step", st)
+    return z

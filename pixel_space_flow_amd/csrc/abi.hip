@@ -1,0 +1,201 @@
+// C ABI of libneo: host-side validation, then one launch per call on the caller's
+// stream.  Declarations and the contract of each call are in include/neo.h.
+#include "neo.h"
+#include "neo_internal.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+namespace {
+
+thread_local char g_err[512];
+
+neo_status fail(neo_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+neo_status ok() {
+  g_err[0] = '\0';
+  return NEO_OK;
+}
+
+neo_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(NEO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool finite(float x) { return isfinite(x); }
+
+size_t dtype_size(neo_dtype d) { return d == NEO_BF16 ? 2 : 4; }
+
+// [a, a+na) and [b, b+nb) share a byte
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// element count t * h * 128 without int64 overflow
+bool rows_fit(int64_t t, int64_t h) {
+  return t >= 0 && h >= 1 && t <= (int64_t)(INT64_MAX / 4) / h / neo::kHeadDim;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* neo_status_string(neo_status s) {
+  switch (s) {
+    case NEO_OK: return "ok";
+    case NEO_ERR_NULL: return "null pointer";
+    case NEO_ERR_SHAPE: return "bad shape";
+    case NEO_ERR_VALUE: return "bad value";
+    case NEO_ERR_UNSUPPORTED: return "unsupported";
+    case NEO_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* neo_last_error(void) { return g_err; }
+
+neo_status neo_qknorm_rope3(const void* q_in, const void* k_in, void* q_out, void* k_out,
+                            int64_t T, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                            const float* q_norm_w, const float* q_norm_hw_w,
+                            const float* k_norm_w, const float* k_norm_hw_w,
+                            const int32_t* pos_thw, float rope_theta, float rope_theta_hw,
+                            float eps, neo_dtype dtype, void* hip_stream) {
+  if (dtype != NEO_F32 && dtype != NEO_BF16)
+    return fail(NEO_ERR_UNSUPPORTED, "neo_qknorm_rope3: unknown dtype %d", (int)dtype);
+  if (head_dim != NEO_HEAD_DIM)
+    return fail(NEO_ERR_SHAPE, "neo_qknorm_rope3: head_dim must be 128, got %d", head_dim);
+  if (Hq < 1 || Hkv < 1)
+    return fail(NEO_ERR_SHAPE, "neo_qknorm_rope3: Hq=%d Hkv=%d must be >= 1", Hq, Hkv);
+  if (T < 0 || !rows_fit(T, Hq) || !rows_fit(T, Hkv))
+    return fail(NEO_ERR_SHAPE, "neo_qknorm_rope3: T=%lld out of range", (long long)T);
+  if (!finite(rope_theta) || rope_theta <= 0.0f || !finite(rope_theta_hw) ||
+      rope_theta_hw <= 0.0f)
+    return fail(NEO_ERR_VALUE, "neo_qknorm_rope3: rope bases must be finite and > 0");
+  if (!finite(eps) || eps < 0.0f)
+    return fail(NEO_ERR_VALUE, "neo_qknorm_rope3: eps must be finite and >= 0");
+  if (T == 0) return ok();
+  if (!q_in || !k_in || !q_out || !k_out || !q_norm_w || !q_norm_hw_w || !k_norm_w ||
+      !k_norm_hw_w || !pos_thw)
+    return fail(NEO_ERR_NULL, "neo_qknorm_rope3: a required pointer is NULL");
+  if (!aligned16(q_in) || !aligned16(k_in) || !aligned16(q_out) || !aligned16(k_out))
+    return fail(NEO_ERR_VALUE, "neo_qknorm_rope3: q/k buffers must be 16-byte aligned");
+  const size_t es = dtype_size(dtype);
+  const size_t qb = (size_t)T * Hq * NEO_HEAD_DIM * es, kb = (size_t)T * Hkv * NEO_HEAD_DIM * es;
+  if ((q_out != q_in && overlap(q_out, qb, q_in, qb)) || overlap(q_out, qb, k_in, kb) ||
+      (k_out != k_in && overlap(k_out, kb, k_in, kb)) || overlap(k_out, kb, q_in, qb) ||
+      overlap(q_out, qb, k_out, kb))
+    return fail(NEO_ERR_VALUE, "neo_qknorm_rope3: outputs overlap inputs other than in place");
+  return from_hip(neo::launch_qknorm_rope3(dtype == NEO_BF16, q_in, k_in, q_out, k_out, T, Hq,
+                                           Hkv, q_norm_w, q_norm_hw_w, k_norm_w, k_norm_hw_w,
+                                           pos_thw, (double)rope_theta, (double)rope_theta_hw,
+                                           eps, static_cast<hipStream_t>(hip_stream)),
+                  "neo_qknorm_rope3 launch");
+}
+
+neo_status neo_gen_attn_fwd(const void* q, const void* k_img, const void* v_img,
+                            const void* k_prefix, const void* v_prefix,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_prefix,
+                            int32_t B, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                            int64_t total_q, int64_t total_prefix, int32_t max_seqlen_q,
+                            int32_t max_seqlen_prefix, float softmax_scale, void* out, float* lse,
+                            neo_dtype dtype, void* hip_stream) {
+  if (dtype != NEO_F32 && dtype != NEO_BF16)
+    return fail(NEO_ERR_UNSUPPORTED, "neo_gen_attn_fwd: unknown dtype %d", (int)dtype);
+  if (head_dim != NEO_HEAD_DIM)
+    return fail(NEO_ERR_SHAPE, "neo_gen_attn_fwd: head_dim must be 128, got %d", head_dim);
+  if (B < 1 || Hq < 1 || Hkv < 1)
+    return fail(NEO_ERR_SHAPE, "neo_gen_attn_fwd: B=%d Hq=%d Hkv=%d must be >= 1", B, Hq, Hkv);
+  if (Hq % Hkv != 0)
+    return fail(NEO_ERR_SHAPE, "neo_gen_attn_fwd: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (max_seqlen_q < 0 || max_seqlen_prefix < 0)
+    return fail(NEO_ERR_SHAPE, "neo_gen_attn_fwd: negative max_seqlen");
+  if (!rows_fit(total_q, Hq) || !rows_fit(total_prefix, Hkv))
+    return fail(NEO_ERR_SHAPE, "neo_gen_attn_fwd: total_q=%lld total_prefix=%lld out of range",
+                (long long)total_q, (long long)total_prefix);
+  if (max_seqlen_q > total_q || max_seqlen_prefix > total_prefix)
+    return fail(NEO_ERR_SHAPE, "neo_gen_attn_fwd: max_seqlen exceeds the tensor's rows");
+  if (!isfinite(softmax_scale))
+    return fail(NEO_ERR_VALUE, "neo_gen_attn_fwd: softmax_scale must be finite");
+  // grid size: one workgroup per (sample, KV head, 4 chunks of 32 query rows), or per
+  // (sample, KV head, 128 query rows) for fp32 -- must fit a 32-bit grid
+  {
+    const int64_t G = Hq / Hkv;
+    const int64_t per = dtype == NEO_BF16 ? ((int64_t)G * ((max_seqlen_q + 31) / 32) + 3) / 4
+                                          : ((int64_t)max_seqlen_q * G + 127) / 128;
+    if (per * Hkv * B >= ((int64_t)1 << 31))
+      return fail(NEO_ERR_SHAPE, "neo_gen_attn_fwd: problem too large for one launch");
+  }
+  if (max_seqlen_q == 0 || total_q == 0) return ok();
+  if (!q || !k_img || !v_img || !cu_seqlens_q || !cu_seqlens_prefix || !out)
+    return fail(NEO_ERR_NULL, "neo_gen_attn_fwd: a required pointer is NULL");
+  if (total_prefix > 0 && (!k_prefix || !v_prefix))
+    return fail(NEO_ERR_NULL, "neo_gen_attn_fwd: k_prefix/v_prefix NULL with total_prefix > 0");
+  const void* bufs[5] = {q, k_img, v_img, k_prefix, v_prefix};
+  for (const void* p : bufs)
+    if (p && !aligned16(p))
+      return fail(NEO_ERR_VALUE, "neo_gen_attn_fwd: q/k/v buffers must be 16-byte aligned");
+  if (!aligned16(out))
+    return fail(NEO_ERR_VALUE, "neo_gen_attn_fwd: out must be 16-byte aligned");
+  const size_t es = dtype_size(dtype);
+  const size_t ob = (size_t)total_q * Hq * NEO_HEAD_DIM * es;
+  const size_t sizes[5] = {ob, (size_t)total_q * Hkv * NEO_HEAD_DIM * es,
+                           (size_t)total_q * Hkv * NEO_HEAD_DIM * es,
+                           (size_t)total_prefix * Hkv * NEO_HEAD_DIM * es,
+                           (size_t)total_prefix * Hkv * NEO_HEAD_DIM * es};
+  const size_t lb = lse ? (size_t)total_q * Hq * sizeof(float) : 0;
+  for (int i = 0; i < 5; ++i)
+    if (bufs[i] && (overlap(out, ob, bufs[i], sizes[i]) || (lse && overlap(lse, lb, bufs[i], sizes[i]))))
+      return fail(NEO_ERR_VALUE, "neo_gen_attn_fwd: out/lse overlap an input");
+  if (lse && overlap(lse, lb, out, ob))
+    return fail(NEO_ERR_VALUE, "neo_gen_attn_fwd: lse overlaps out");
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)NEO_HEAD_DIM);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipError_t e;
+  if (dtype == NEO_BF16)
+    e = neo::launch_gen_attn_bf16(q, k_img, v_img, k_prefix, v_prefix, cu_seqlens_q,
+                                  cu_seqlens_prefix, B, Hq, Hkv, max_seqlen_q, max_seqlen_prefix,
+                                  scale, out, lse, total_q, total_prefix, stream);
+  else
+    e = neo::launch_gen_attn_f32(
+        static_cast<const float*>(q), static_cast<const float*>(k_img),
+        static_cast<const float*>(v_img), static_cast<const float*>(k_prefix),
+        static_cast<const float*>(v_prefix), cu_seqlens_q, cu_seqlens_prefix, B, Hq, Hkv,
+        max_seqlen_q, max_seqlen_prefix, scale, static_cast<float*>(out), lse, total_q,
+        total_prefix, stream);
+  return from_hip(e, "neo_gen_attn_fwd launch");
+}
+
+neo_status neo_fm_euler_step(float* z, const float* x0_pred, int64_t n, float t, float t_next,
+                             float t_eps, void* hip_stream) {
+  if (n < 0 || n > INT64_MAX / 16)
+    return fail(NEO_ERR_SHAPE, "neo_fm_euler_step: n=%lld out of range", (long long)n);
+  if (!finite(t) || !finite(t_next) || !finite(t_eps))
+    return fail(NEO_ERR_VALUE, "neo_fm_euler_step: t, t_next, t_eps must be finite");
+  if (t_eps <= 0.0f) return fail(NEO_ERR_VALUE, "neo_fm_euler_step: t_eps must be > 0");
+  if (t_next < t) return fail(NEO_ERR_VALUE, "neo_fm_euler_step: t_next < t");
+  if (n == 0) return ok();
+  if (!z || !x0_pred) return fail(NEO_ERR_NULL, "neo_fm_euler_step: z or x0_pred is NULL");
+  const size_t nb = (size_t)n * sizeof(float);
+  if (static_cast<const void*>(z) != static_cast<const void*>(x0_pred) &&
+      overlap(z, nb, x0_pred, nb))
+    return fail(NEO_ERR_VALUE, "neo_fm_euler_step: z and x0_pred partially overlap");
+  if ((reinterpret_cast<uintptr_t>(z) | reinterpret_cast<uintptr_t>(x0_pred)) & 3)
+    return fail(NEO_ERR_VALUE, "neo_fm_euler_step: buffers must be 4-byte aligned");
+  const double denom = fmax(1.0 - (double)t, (double)t_eps);
+  const float coef = (float)(((double)t_next - (double)t) / denom);
+  return from_hip(neo::launch_euler_step(z, x0_pred, n, coef, static_cast<hipStream_t>(hip_stream)),
+                  "neo_fm_euler_step launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Internal declarations shared by the HIP translation units of libneo.
+// Nothing here is part of the public ABI (that is include/neo.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace neo {
+
+constexpr int kHeadDim = 128;
+constexpr int kHalfDim = 64;
+
+// ---- launchers (host side); each returns the hipError_t of its launch --------------
+
+hipError_t launch_qknorm_rope3(bool bf16, const void* q_in, const void* k_in, void* q_out,
+                               void* k_out, int64_t T, int Hq, int Hkv, const float* wq_t,
+                               const float* wq_hw, const float* wk_t, const float* wk_hw,
+                               const int32_t* pos, double theta, double theta_hw, float eps,
+                               hipStream_t stream);
+
+hipError_t launch_gen_attn_bf16(const void* q, const void* k_img, const void* v_img,
+                                const void* k_pre, const void* v_pre, const int32_t* cu_q,
+                                const int32_t* cu_p, int B, int Hq, int Hkv, int max_q,
+                                int max_p, float scale, void* out, float* lse, int64_t Tq,
+                                int64_t Tp, hipStream_t stream);
+
+hipError_t launch_gen_attn_f32(const float* q, const float* k_img, const float* v_img,
+                               const float* k_pre, const float* v_pre, const int32_t* cu_q,
+                               const int32_t* cu_p, int B, int Hq, int Hkv, int max_q, int max_p,
+                               float scale, float* out, float* lse, int64_t Tq, int64_t Tp,
+                               hipStream_t stream);
+
+hipError_t launch_euler_step(float* z, const float* x0, int64_t n, float coef,
+                             hipStream_t stream);
+
+// ---- device helpers -----------------------------------------------------------------
+
+// bf16 <-> fp32 on raw 16-bit patterns.  The conversion to bf16 rounds to nearest
+// even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// XCD-aware remap of the linear workgroup id.  Workgroups are handed to the 8 XCDs
+// round-robin, so consecutive logical ids would land on different L2s.  This maps the
+// hardware order onto contiguous logical ranges per XCD, so workgroups that read the
+// same K/V run behind the same L2.  A bijection for any total count.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t lin, uint32_t total) {
+  constexpr uint32_t kXcd = 8;
+  uint32_t q = total / kXcd, r = total % kXcd;
+  uint32_t xcd = lin % kXcd, idx = lin / kXcd;
+  return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+}
+
+}  // namespace neo

@@ -1,0 +1,334 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Every case feeds both sides the same seeded inputs and compares element by
+element; at the full workload sizes the attention output is compared on sampled
+query rows that the oracle evaluates one by one.  Tolerances (per call):
+fp32 max-abs <= 1e-4; bf16 max-abs <= 2e-2 and relative L2 <= 5e-3.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    return torch
+
+
+def _say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def neo():
+    _cuda()
+    import pixel_space_flow_amd as P
+    P.lib()  # raises if the library is missing
+    return P
+
+
+# --------------------------------------------------------------------------------------
+# Euler step
+# --------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", W.CONFIG_NAMES)
+def test_euler_configs(neo, name):
+    torch = _cuda()
+    w = W.make(name)
+    t, tn = w.t_grid[0], w.t_grid[1]
+    z0 = w.z_start if w.z_start is not None else (np.float32(w.sigma_R) * w.eps_pixels)
+    z0 = z0.astype(np.float32)
+    _say(f"euler {name} n={z0.size} t={t}->{tn}")
+    z = H.dev_f32(z0)
+    x = H.dev_f32(w.x_hat)
+    neo.fm_euler_step(z, x, t, tn, w.t_eps)
+    torch.cuda.synchronize()
+    ref = oracle.euler_step(z0, w.x_hat, t, tn, w.t_eps)
+    H.assert_close(H.host(z), ref, "f32", f"euler {name}")
+
+
+def test_euler_trajectory_small(neo):
+    """8 steps with x0 fixed to the clean image stay on z_t = t x + (1-t) sigma eps."""
+    torch = _cuda()
+    w = W.make("small")
+    z0 = (np.float32(w.sigma_R) * w.eps_pixels).astype(np.float32)
+    z = H.dev_f32(z0)
+    x = H.dev_f32(w.x_hat)
+    zr = z0.astype(np.float64)
+    for k in range(len(w.t_grid) - 1):
+        t, tn = w.t_grid[k], w.t_grid[k + 1]
+        _say(f"euler trajectory step {k}")
+        neo.fm_euler_step(z, x, t, tn, w.t_eps)
+        zr = oracle.euler_step(zr, w.x_hat, t, tn, w.t_eps)
+        torch.cuda.synchronize()
+        got = H.host(z)
+        H.assert_close(got, zr, "f32", f"trajectory step {k}")
+        closed = tn * w.x_hat.astype(np.float64) + (1 - tn) * w.sigma_R * w.eps_pixels
+        assert np.max(np.abs(got - closed)) < 1e-4
+    np.testing.assert_allclose(H.host(z), w.x_hat, atol=1e-5)
+
+
+def test_euler_edges(neo):
+    """Clamp branch, a length that is not a multiple of 4, an unaligned start, n = 0."""
+    torch = _cuda()
+    rng = np.random.default_rng(3)
+    for n, off, t, tn in ((1003, 0, 0.99, 1.0), (4099, 1, 0.25, 0.3), (7, 3, 0.0, 0.05),
+                          (1, 0, 0.5, 0.5)):
+        _say(f"euler edge n={n} offset={off}")
+        z0 = rng.standard_normal(n + off).astype(np.float32)
+        x0 = rng.standard_normal(n + off).astype(np.float32)
+        zb, xb = H.dev_f32(z0), H.dev_f32(x0)
+        neo.fm_euler_step(zb[off:], xb[off:], t, tn, 0.02)
+        torch.cuda.synchronize()
+        ref = oracle.euler_step(z0[off:], x0[off:], t, tn, 0.02)
+        got = H.host(zb)
+        H.assert_close(got[off:], ref, "f32", f"euler edge n={n}")
+        np.testing.assert_array_equal(got[:off], z0[:off])
+    empty = torch.empty(0, device="cuda")
+    neo.fm_euler_step(empty, empty, 0.1, 0.2)
+
+
+# --------------------------------------------------------------------------------------
+# Norm + rotary prologue
+# --------------------------------------------------------------------------------------
+
+def _prologue_ref(w):
+    return oracle.qknorm_rope3(w.q, w.k, w.wq_t, w.wq_hw, w.wk_t, w.wk_hw, w.pos_img,
+                               w.rope_theta, w.rope_theta_hw, w.eps)
+
+
+def _prologue_gpu(neo, w, in_place=False):
+    q, k = H.dev(w.q, w.dtype), H.dev(w.k, w.dtype)
+    args = (H.dev_f32(w.wq_t), H.dev_f32(w.wq_hw), H.dev_f32(w.wk_t), H.dev_f32(w.wk_hw),
+            H.dev_i32(w.pos_img), w.rope_theta, w.rope_theta_hw, w.eps)
+    if in_place:
+        return neo.qknorm_rope3(q, k, *args, q_out=q, k_out=k)
+    return neo.qknorm_rope3(q, k, *args)
+
+
+@pytest.mark.parametrize("name", W.CONFIG_NAMES)
+def test_prologue_configs(neo, name):
+    torch = _cuda()
+    w = W.make(name, pixels=False)
+    _say(f"prologue {name} T={w.Tq} Hq={w.Hq} Hkv={w.Hkv} {w.dtype}")
+    qo, ko = _prologue_gpu(neo, w)
+    torch.cuda.synchronize()
+    qr, kr = _prologue_ref(w)
+    H.assert_close(H.host(qo), qr, w.dtype, f"prologue q {name}")
+    H.assert_close(H.host(ko), kr, w.dtype, f"prologue k {name}")
+    if w.dtype == "bf16":
+        # one rounding: every element is within half a bf16 ulp of the fp64 value (plus
+        # the fp32 arithmetic error), i.e. at most 2^-8 relative
+        got = H.host(qo).astype(np.float64)
+        assert np.all(np.abs(got - qr) <= np.abs(qr) * 2.0 ** -8 + 1e-6)
+
+
+def test_prologue_in_place(neo):
+    torch = _cuda()
+    w = W.make("small", pixels=False)
+    _say("prologue in place")
+    qo, ko = _prologue_gpu(neo, w, in_place=True)
+    torch.cuda.synchronize()
+    qr, kr = _prologue_ref(w)
+    H.assert_close(H.host(qo), qr, "bf16", "in-place q")
+    H.assert_close(H.host(ko), kr, "bf16", "in-place k")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,Hq,Hkv", [(1, 1, 1), (5, 3, 1), (33, 6, 2), (7, 32, 8), (3, 16, 16)])
+def test_prologue_shapes(neo, dtype, T, Hq, Hkv):
+    """Row counts that leave the last 4-row group partly empty; large positions."""
+    torch = _cuda()
+    rng = np.random.default_rng(T * 100 + Hq)
+    q = H.round_to(rng.standard_normal((T, Hq, 128)) * 3, dtype)
+    k = H.round_to(rng.standard_normal((T, Hkv, 128)) * 0.01, dtype)
+    ws = [rng.uniform(0.5, 1.5, 64).astype(np.float32) for _ in range(4)]
+    pos = np.stack([rng.integers(0, 20000, T), rng.integers(0, 256, T),
+                    rng.integers(0, 256, T)]).astype(np.int32)
+    _say(f"prologue shape T={T} Hq={Hq} Hkv={Hkv} {dtype}")
+    qo, ko = neo.qknorm_rope3(H.dev(q, dtype), H.dev(k, dtype), *[H.dev_f32(x) for x in ws],
+                              H.dev_i32(pos), 5e6, 1e4, 1e-6)
+    torch.cuda.synchronize()
+    qr, kr = oracle.qknorm_rope3(q, k, *ws, pos, 5e6, 1e4, 1e-6)
+    H.assert_close(H.host(qo), qr, dtype, "q")
+    H.assert_close(H.host(ko), kr, dtype, "k")
+
+
+def test_prologue_empty(neo):
+    torch = _cuda()
+    e = torch.empty((0, 4, 128), device="cuda", dtype=torch.bfloat16)
+    w = torch.ones(64, device="cuda")
+    neo.qknorm_rope3(e, e[:, :1].contiguous(), w, w, w, w,
+                     torch.empty((3, 0), dtype=torch.int32, device="cuda"))
+
+
+# --------------------------------------------------------------------------------------
+# Attention
+# --------------------------------------------------------------------------------------
+
+def _attn_inputs(w):
+    """Identical inputs for both sides: rotated q/k (the oracle's, rounded), raw v."""
+    qr, kr = _prologue_ref(w)
+    q = H.round_to(qr, w.dtype)
+    k = H.round_to(kr, w.dtype)
+    kp, vp = H.frozen_prefix(w)
+    return q, k, w.v, kp, vp
+
+
+def _attn_gpu(neo, w, q, k, v, kp, vp, return_lse=True):
+    d = w.dtype
+    return neo.gen_attn_fwd(H.dev(q, d), H.dev(k, d), H.dev(v, d), H.dev(kp, d), H.dev(vp, d),
+                            H.dev_i32(w.cu_q), H.dev_i32(w.cu_p), max(w.n_img), max(w.n_prefix),
+                            return_lse=return_lse)
+
+
+def _sample_rows(w, n_per_sample, rng):
+    rows = []
+    for b in range(w.B):
+        a, e = int(w.cu_q[b]), int(w.cu_q[b + 1])
+        pick = {a, e - 1, a + 31, a + 32, e - 33} | set(rng.integers(a, e, n_per_sample).tolist())
+        rows += sorted(r for r in pick if a <= r < e)
+    return np.array(rows, dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "mid"])
+def test_attn_configs_full(neo, name):
+    torch = _cuda()
+    w = W.make(name, pixels=False)
+    q, k, v, kp, vp = _attn_inputs(w)
+    _say(f"attention {name} Tq={w.Tq} Tp={w.Tp} {w.dtype}")
+    out, lse = _attn_gpu(neo, w, q, k, v, kp, vp)
+    torch.cuda.synchronize()
+    ref, lse_ref = oracle.gen_attn(q, k, v, kp, vp, w.cu_q, w.cu_p, with_lse=True)
+    H.assert_close(H.host(out), ref, w.dtype, f"attention {name}")
+    np.testing.assert_allclose(H.host(lse).T, lse_ref, atol=2e-3 if w.dtype == "bf16" else 1e-5)
+
+
+@pytest.mark.parametrize("name", ["large", "editing"])
+def test_attn_configs_sampled(neo, name):
+    """Full-size workloads in the benchmark's launch configuration; the oracle checks
+    sampled query rows (all heads) including tile edges and each sample's ends."""
+    torch = _cuda()
+    w = W.make(name, pixels=False)
+    q, k, v, kp, vp = _attn_inputs(w)
+    _say(f"attention {name} Tq={w.Tq} Tp={w.Tp} (sampled)")
+    out, lse = _attn_gpu(neo, w, q, k, v, kp, vp)
+    torch.cuda.synchronize()
+    rows = _sample_rows(w, 24, np.random.default_rng(0))
+    ref, lse_ref = oracle.gen_attn(q, k, v, kp, vp, w.cu_q, w.cu_p, tokens=rows, with_lse=True)
+    got = H.host(out)[rows]
+    H.assert_close(got, ref, "bf16", f"attention {name} sampled")
+    np.testing.assert_allclose(H.host(lse).T[rows], lse_ref, atol=2e-3)
+    assert np.all(np.isfinite(H.host(out)))
+
+
+def _random_case(rng, n_img, n_pre, Hq, Hkv, dtype, wscale=1.0):
+    Tq, Tp = sum(n_img), sum(n_pre)
+    f = lambda *s: H.round_to(rng.standard_normal(s) * wscale, dtype)
+    return dict(q=f(Tq, Hq, 128), k=f(Tq, Hkv, 128), v=H.round_to(rng.standard_normal((Tq, Hkv, 128)), dtype),
+                kp=f(Tp, Hkv, 128), vp=H.round_to(rng.standard_normal((Tp, Hkv, 128)), dtype),
+                cu_q=np.concatenate([[0], np.cumsum(n_img)]).astype(np.int32),
+                cu_p=np.concatenate([[0], np.cumsum(n_pre)]).astype(np.int32))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n_img,n_pre,Hq,Hkv", [
+    ([37], [0], 4, 1),            # no prefix, ragged query block
+    ([1], [1], 8, 2),             # single query, two keys
+    ([100, 3, 64], [65, 130, 0], 8, 2),   # ragged batch, tiles straddling the boundary
+    ([50, 0, 29], [10, 7, 1], 4, 4),      # an empty sample, MHA
+    ([40], [200], 6, 2),          # G = 3
+    ([96], [33], 16, 2),          # G = 8: 4 waves x 2 heads per chunk group
+    ([257], [511], 32, 8),        # odd lengths on the production head shape
+])
+def test_attn_edges(neo, dtype, n_img, n_pre, Hq, Hkv):
+    torch = _cuda()
+    rng = np.random.default_rng(sum(n_img) * 7 + sum(n_pre) + Hq)
+    c = _random_case(rng, n_img, n_pre, Hq, Hkv, dtype, wscale=0.5)
+    _say(f"attention edge n_img={n_img} n_pre={n_pre} Hq={Hq} Hkv={Hkv} {dtype}")
+    d = dtype
+    out, lse = neo.gen_attn_fwd(H.dev(c["q"], d), H.dev(c["k"], d), H.dev(c["v"], d),
+                                H.dev(c["kp"], d), H.dev(c["vp"], d), H.dev_i32(c["cu_q"]),
+                                H.dev_i32(c["cu_p"]), max(n_img), max(n_pre), return_lse=True)
+    torch.cuda.synchronize()
+    ref, lse_ref = oracle.gen_attn(c["q"], c["k"], c["v"], c["kp"], c["vp"], c["cu_q"], c["cu_p"],
+                                   with_lse=True)
+    H.assert_close(H.host(out), ref, dtype, "attention edge")
+    np.testing.assert_allclose(H.host(lse).T, lse_ref, atol=2e-3 if dtype == "bf16" else 1e-5)
+
+
+def test_attn_peaky_softmax(neo):
+    """Large-norm queries and keys make the softmax peaky (the lazy rescale path is
+    exercised on later tiles and score errors are not averaged away)."""
+    torch = _cuda()
+    rng = np.random.default_rng(77)
+    c = _random_case(rng, [300, 200], [700, 64], 32, 8, "bf16", wscale=3.0)
+    _say("attention peaky")
+    out = neo.gen_attn_fwd(H.dev(c["q"], "bf16"), H.dev(c["k"], "bf16"), H.dev(c["v"], "bf16"),
+                           H.dev(c["kp"], "bf16"), H.dev(c["vp"], "bf16"), H.dev_i32(c["cu_q"]),
+                           H.dev_i32(c["cu_p"]), 300, 700)
+    torch.cuda.synchronize()
+    ref = oracle.gen_attn(c["q"], c["k"], c["v"], c["kp"], c["vp"], c["cu_q"], c["cu_p"])
+    H.assert_close(H.host(out), ref, "bf16", "peaky")
+
+
+def test_attn_no_prefix_buffers(neo):
+    """Tp = 0: the prefix tensors are empty and no prefix pointer is passed."""
+    torch = _cuda()
+    rng = np.random.default_rng(5)
+    c = _random_case(rng, [70], [0], 4, 1, "bf16")
+    e = torch.empty((0, 1, 128), dtype=torch.bfloat16, device="cuda")
+    out = neo.gen_attn_fwd(H.dev(c["q"], "bf16"), H.dev(c["k"], "bf16"), H.dev(c["v"], "bf16"),
+                           e, e, H.dev_i32(c["cu_q"]), H.dev_i32(c["cu_p"]), 70, 0)
+    torch.cuda.synchronize()
+    ref = oracle.gen_attn(c["q"], c["k"], c["v"], c["kp"], c["vp"], c["cu_q"], c["cu_p"])
+    H.assert_close(H.host(out), ref, "bf16", "no prefix")
+
+
+def test_attn_long_sample(neo):
+    """A maximum-size single sample: 16384 image tokens over a 2048-token prefix
+    (the 4096x4096-pixel image); sampled rows."""
+    torch = _cuda()
+    rng = np.random.default_rng(8)
+    c = _random_case(rng, [16384], [2048], 32, 8, "bf16")
+    _say("attention long sample 16384 + 2048")
+    out = neo.gen_attn_fwd(H.dev(c["q"], "bf16"), H.dev(c["k"], "bf16"), H.dev(c["v"], "bf16"),
+                           H.dev(c["kp"], "bf16"), H.dev(c["vp"], "bf16"), H.dev_i32(c["cu_q"]),
+                           H.dev_i32(c["cu_p"]), 16384, 2048)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 31, 32, 5000, 8191, 8192, 16383], dtype=np.int64)
+    ref = oracle.gen_attn(c["q"], c["k"], c["v"], c["kp"], c["vp"], c["cu_q"], c["cu_p"],
+                          tokens=rows)
+    H.assert_close(H.host(out)[rows], ref, "bf16", "long sample")
+
+
+# --------------------------------------------------------------------------------------
+# The block: prologue -> attention, each workload, against the fp64 chain
+# --------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", W.CONFIG_NAMES)
+def test_block_end_to_end(neo, name):
+    torch = _cuda()
+    w = W.make(name, pixels=False)
+    kp, vp = H.frozen_prefix(w)
+    _say(f"block {name}")
+    qo, ko = _prologue_gpu(neo, w)
+    d = w.dtype
+    out = neo.gen_attn_fwd(qo, ko, H.dev(w.v, d), H.dev(kp, d), H.dev(vp, d), H.dev_i32(w.cu_q),
+                           H.dev_i32(w.cu_p), max(w.n_img), max(w.n_prefix))
+    torch.cuda.synchronize()
+    qr, kr = _prologue_ref(w)
+    rows = None if w.Tq <= 1024 else _sample_rows(w, 16, np.random.default_rng(1))
+    ref = oracle.gen_attn(qr, kr, w.v, kp, vp, w.cu_q, w.cu_p, tokens=rows)
+    got = H.host(out) if rows is None else H.host(out)[rows]
+    H.assert_close(got, ref, d, f"block {name}")
