@@ -21,9 +21,10 @@
 //     score accumulator to the second MFMA without any data movement.  V is staged in
 //     LDS transposed ([dim][key]) so each lane reads its keys with two 8-byte loads;
 //   * online softmax in fp32 on exp2 with the 1/sqrt(d) * log2(e) scale folded into one
-//     FMA.  The running maximum is raised only when a tile's maximum exceeds it by more
-//     than 2^8, so the O rescale (64 multiplies per lane) runs on the first tile and
-//     almost never afterwards, while every exponent stays <= 2^8; the final O / l is
+//     FMA; the row sum adds the bf16-rounded weights that the PV product uses.  The
+//     running maximum is raised only when a tile's maximum exceeds it by more than 2^8,
+//     so the O rescale (64 multiplies per lane) runs on the first tile and almost never
+//     afterwards, while every exponent stays <= 2^8; the final O / l is
 //     the same quotient whichever reference maximum was used;
 //   * K/V tiles of 64 keys are double-buffered in LDS (2 x 34 KB); the next tile's
 //     global loads are issued before the current tile's MFMAs and written to the other
@@ -42,6 +43,7 @@ namespace neo {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
@@ -53,6 +55,7 @@ constexpr int kKTile = kBN * kKS;            // bf16 elements
 constexpr int kVTile = kHeadDim * kVS;       // bf16 elements
 constexpr int kStage = kKTile + kVTile;      // one K + V^T stage
 constexpr float kTau = 8.0f;                 // lazy-rescale threshold (log2 units)
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 struct TileRegs {
   uint4 k[4];
@@ -235,21 +238,23 @@ __global__ __launch_bounds__(kThreads, 2) void gen_attn_bf16_kernel(
           for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
         m = mnew;
       }
+      // P in bf16; the row sum adds the same rounded weights (v_dot2 against (1, 1)),
+      // so the normalised weights sum to one exactly and a near one-hot softmax
+      // returns the dominant value without the weight's rounding error
       bf16x8 pb[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        uint4 pk;
-        float pv[8];
+        uint32_t pk[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pv[e] = __builtin_amdgcn_exp2f(fmaf(s[u >> 1][(u & 1) * 8 + e], scale_log2, -m));
-          lsum += pv[e];
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[u >> 1][(u & 1) * 8 + e], scale_log2, -m));
+          const float p1 =
+              __builtin_amdgcn_exp2f(fmaf(s[u >> 1][(u & 1) * 8 + e + 1], scale_log2, -m));
+          pk[e >> 1] = pack_bf16x2(p0, p1);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e >> 1]), kOnes2,
+                                                 lsum, false);
         }
-        pk.x = pack_bf16x2(pv[0], pv[1]);
-        pk.y = pack_bf16x2(pv[2], pv[3]);
-        pk.z = pack_bf16x2(pv[4], pv[5]);
-        pk.w = pack_bf16x2(pv[6], pv[7]);
-        pb[u] = as_bf16x8(pk);
+        pb[u] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
       }
       // O^T += V^T P^T: k-slot (hl, e) of step u is key 32*(u/2) + 16*(u%2) + 4*hl + 8*(e/4) + e%4
 #pragma unroll

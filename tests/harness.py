@@ -49,6 +49,7 @@ def assert_close(got, ref, dtype: str, what: str = ""):
     assert max_abs <= tol["max_abs"], f"{what}: max-abs {max_abs:.3e} > {tol['max_abs']:.1e}"
     if tol["rel_l2"] is not None:
         assert rel <= tol["rel_l2"], f"{what}: rel-L2 {rel:.3e} > {tol['rel_l2']:.1e}"
+    print(f"[parity] {what}: max-abs {max_abs:.3e} rel-L2 {rel:.3e}", flush=True)
     return max_abs, rel
 
 
