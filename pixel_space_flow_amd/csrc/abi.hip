@@ -127,11 +127,11 @@ neo_status neo_gen_attn_fwd(const void* q, const void* k_img, const void* v_img,
     return fail(NEO_ERR_SHAPE, "neo_gen_attn_fwd: max_seqlen exceeds the tensor's rows");
   if (!isfinite(softmax_scale))
     return fail(NEO_ERR_VALUE, "neo_gen_attn_fwd: softmax_scale must be finite");
-  // grid size: one workgroup per (sample, KV head, 4 chunks of 32 query rows), or per
+  // grid size: one workgroup per (sample, KV head, 8 chunks of 32 query rows), or per
   // (sample, KV head, 128 query rows) for fp32 -- must fit a 32-bit grid
   {
     const int64_t G = Hq / Hkv;
-    const int64_t per = dtype == NEO_BF16 ? ((int64_t)G * ((max_seqlen_q + 31) / 32) + 3) / 4
+    const int64_t per = dtype == NEO_BF16 ? ((int64_t)G * ((max_seqlen_q + 31) / 32) + 7) / 8
                                           : ((int64_t)max_seqlen_q * G + 127) / 128;
     if (per * Hkv * B >= ((int64_t)1 << 31))
       return fail(NEO_ERR_SHAPE, "neo_gen_attn_fwd: problem too large for one launch");

@@ -8,28 +8,33 @@
 // ("SenseNova-U1 ... NEO-unify Architecture" paper notes, §4.4 KV cache reuse); the
 // prefix and the image block are two separate segments read in place, no concatenation.
 //
-// bf16 kernel (the production path), one workgroup of 4 waves per
-// (sample, KV head, group of 4 chunks); a chunk is 32 query tokens of one query head:
-//   * the 4 chunks of a workgroup share one KV head, so every K/V tile staged in LDS
-//     feeds 4 waves (with Hq/Hkv = 4 these are the 4 query heads of one KV group over
-//     the same 32 tokens);
+// bf16 kernel (the production path): one workgroup of 8 waves per (sample, KV head,
+// group of 8 chunks); a chunk is 32 query tokens of one query head.
+//   * the 8 chunks of a workgroup share one KV head, so every K/V tile staged in LDS
+//     feeds 8 waves (with Hq/Hkv = 4: the 4 query heads of one KV group over 64 tokens);
 //   * scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: A = a
 //     32-key slice of the K tile (rows = keys), B = the wave's Q^T held in registers.
 //     In the 32x32 accumulator layout each lane then holds one query (lane % 32) and
 //     16 keys, so the softmax row statistics are in-lane plus one swap with lane ^ 32;
 //   * the same layout is exactly the B operand of O^T = V^T P^T, so P goes from the
-//     score accumulator to the second MFMA without any data movement.  V is staged in
-//     LDS transposed ([dim][key]) so each lane reads its keys with two 8-byte loads;
+//     score accumulator to the second MFMA without any data movement.  V stays
+//     row-major in LDS and is read with ds_read_b64_tr_b16, whose 16-lane transpose
+//     hands each lane 4 consecutive keys of one dim;
+//   * LDS rows are XOR-swizzled at 16-byte granularity (no padding), which keeps the
+//     staging writes, the K reads and the transposed V reads free of bank conflicts;
+//   * waves w and w+4 share a SIMD; the upper four run half a tile behind (the PV
+//     product of the previous tile first), so one wave's softmax overlaps the other's
+//     matrix products instead of both waves contending for the same unit at once;
 //   * online softmax in fp32 on exp2 with the 1/sqrt(d) * log2(e) scale folded into one
 //     FMA; the row sum adds the bf16-rounded weights that the PV product uses.  The
 //     running maximum is raised only when a tile's maximum exceeds it by more than 2^8,
 //     so the O rescale (64 multiplies per lane) runs on the first tile and almost never
-//     afterwards, while every exponent stays <= 2^8; the final O / l is
-//     the same quotient whichever reference maximum was used;
-//   * K/V tiles of 64 keys are double-buffered in LDS (2 x 34 KB); the next tile's
-//     global loads are issued before the current tile's MFMAs and written to the other
-//     buffer afterwards, one barrier per tile;
-//   * key rows past the sample's end are zero-filled and their scores set to -inf;
+//     afterwards, while every exponent stays <= 2^8; the final O / l is the same
+//     quotient whichever reference maximum was used;
+//   * K/V tiles of 64 keys from raw buffer loads: the resource of each tile ends at its
+//     segment's end, so rows past it read as zeros (their scores are then set to -inf)
+//     with no per-row address arithmetic.  Three LDS stages; the next tile's loads are
+//     in flight during the current tile's math, one barrier per tile;
 //   * the workgroup order is remapped so each XCD works on contiguous (sample, KV head)
 //     ranges and its L2 holds that head's K/V.
 //
@@ -46,93 +51,80 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kThreads = 512;                // 8 waves, two per SIMD
 constexpr int kWaves = kThreads / 64;
 constexpr int kBN = 64;                      // keys per tile
-constexpr int kKS = kHeadDim + 8;            // K tile row stride (bf16), 272 B
-constexpr int kVS = kBN + 4;                 // V^T tile row stride (bf16), 136 B
-constexpr int kKTile = kBN * kKS;            // bf16 elements
-constexpr int kVTile = kHeadDim * kVS;       // bf16 elements
-constexpr int kStage = kKTile + kVTile;      // one K + V^T stage
+constexpr int kRowBytes = kHeadDim * 2;      // one K or V row in LDS (no padding)
+constexpr int kTileBytes = kBN * kRowBytes;  // 16 KB
+constexpr int kStageBytes = 2 * kTileBytes;  // K tile + V tile
+constexpr int kStages = 3;
 constexpr float kTau = 8.0f;                 // lazy-rescale threshold (log2 units)
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+constexpr int kBufFlags = 0x00020000;        // raw buffer, 32-bit data format (gfx9 family)
 
-struct TileRegs {
-  uint4 k[4];
-  uint4 v[4];
-};
+// LDS tiles hold 64 rows of 16 chunks (16 bytes = 8 dims each).  Chunk c of row r is
+// stored at slot c ^ swz(r), which makes all three access patterns conflict-free:
+// the row-wise 16-byte writes, the K-fragment reads (16 consecutive rows, one chunk)
+// and the transposed V reads (4 consecutive rows, 4 consecutive chunks per half-wave).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
-struct SampleView {
-  const uint16_t* k_pre;
-  const uint16_t* v_pre;
-  const uint16_t* k_img;
-  const uint16_t* v_img;
-  int64_t p0, i0;  // first prefix row, first image row of the sample
-  int P, Lk;       // prefix length, total keys
-  int Hkv, g;
-};
-
-__device__ __forceinline__ uint4 load_key_row(const SampleView& s, const uint16_t* pre,
-                                              const uint16_t* img, int j, int dg) {
-  const uint16_t* row = nullptr;
-  if (j < s.P)
-    row = pre + ((s.p0 + j) * s.Hkv + s.g) * kHeadDim;
-  else if (j < s.Lk)
-    row = img + ((s.i0 + (j - s.P)) * s.Hkv + s.g) * kHeadDim;
-  if (row == nullptr) return make_uint4(0, 0, 0, 0);
-  return *reinterpret_cast<const uint4*>(row + dg * 8);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
+                                           kBufFlags);
 }
 
-// K rows: thread (dg = tid % 16, r = tid / 16) loads rows r, r+16, r+32, r+48.
-// V rows: the same thread loads the 4 consecutive rows 4r..4r+3 (for the transpose).
-__device__ __forceinline__ void load_tile(TileRegs& R, const SampleView& s, int tile, int tid) {
-  const int dg = tid & 15, r = tid >> 4;
-  const int base = tile * kBN;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) R.k[i] = load_key_row(s, s.k_pre, s.k_img, base + r + 16 * i, dg);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) R.v[i] = load_key_row(s, s.v_pre, s.v_img, base + 4 * r + i, dg);
-}
-
-__device__ __forceinline__ uint32_t word(const uint4& u, int w) {
-  return w == 0 ? u.x : (w == 1 ? u.y : (w == 2 ? u.z : u.w));
-}
-
-__device__ __forceinline__ void store_tile(uint16_t* stage, const TileRegs& R, int tid) {
-  const int dg = tid & 15, r = tid >> 4;
-  uint16_t* Ks = stage;
-  uint16_t* VT = stage + kKTile;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<uint4*>(Ks + (r + 16 * i) * kKS + dg * 8) = R.k[i];
-  // transpose: dim 8*dg + e of keys 4r..4r+3 becomes 4 consecutive bf16 of row (8*dg + e)
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int w = e >> 1;
-    const uint32_t a0 = word(R.v[0], w), a1 = word(R.v[1], w);
-    const uint32_t a2 = word(R.v[2], w), a3 = word(R.v[3], w);
-    uint32_t lo, hi;
-    if (e & 1) {
-      lo = (a0 >> 16) | (a1 & 0xffff0000u);
-      hi = (a2 >> 16) | (a3 & 0xffff0000u);
-    } else {
-      lo = (a0 & 0xffffu) | (a1 << 16);
-      hi = (a2 & 0xffffu) | (a3 << 16);
-    }
-    *reinterpret_cast<uint2*>(VT + (dg * 8 + e) * kVS + 4 * r) = make_uint2(lo, hi);
-  }
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-__global__ __launch_bounds__(kThreads, 2) void gen_attn_bf16_kernel(
+// Key segments of one (sample, KV head): the frozen prefix, then the image block.
+struct Segments {
+  const uint8_t* kbase[2];
+  const uint8_t* vbase[2];
+  int len[2];
+  int ntiles[2];
+  int64_t row_bytes;  // Hkv * 128 * 2
+};
+
+// One tile = 64 consecutive rows of one key segment.  The buffer resource starts at the
+// tile's first row and ends at the segment's end, so the hardware range check returns
+// zeros for rows past the segment: no branches and no per-row address arithmetic.
+__device__ __forceinline__ void tile_rsrc(const Segments& S, int it, __amdgpu_buffer_rsrc_t& rk,
+                                          __amdgpu_buffer_rsrc_t& rv) {
+  const int seg = it < S.ntiles[0] ? 0 : 1;
+  const int tl = seg == 0 ? it : it - S.ntiles[0];
+  const int64_t off = (int64_t)tl * kBN * S.row_bytes;
+  const int rows = S.len[seg] - tl * kBN;
+  const int64_t nbytes = (int64_t)(rows < kBN ? rows : kBN) * S.row_bytes;  // < 2^32
+  rk = make_rsrc(S.kbase[seg] + off, nbytes);
+  rv = make_rsrc(S.vbase[seg] + off, nbytes);
+}
+
+__device__ __forceinline__ int tile_valid(const Segments& S, int it) {
+  const int seg = it < S.ntiles[0] ? 0 : 1;
+  const int tl = seg == 0 ? it : it - S.ntiles[0];
+  return S.len[seg] - tl * kBN;
+}
+
+// Staging: thread t moves 16-byte chunks q = t and t + 512 of the K tile and of the V tile
+// (row q / 16, chunk q % 16) from HBM to registers, then to their swizzled LDS slots.
+struct Stage {
+  uint4 k[2], v[2];
+};
+
+__global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_img,
     const uint16_t* __restrict__ v_img, const uint16_t* __restrict__ k_pre,
     const uint16_t* __restrict__ v_pre, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_p, int Hq, int Hkv, int n_cg, int max_q, int max_p,
     int64_t Tq, int64_t Tp, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
 
   const uint32_t id = xcd_remap(blockIdx.x, gridDim.x);
   const int cg = (int)(id % (uint32_t)n_cg);
@@ -156,15 +148,57 @@ __global__ __launch_bounds__(kThreads, 2) void gen_attn_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, col = lane & 31;
+  // waves w and w + 4 share a SIMD; the upper four run half a tile behind (PV of the
+  // previous tile first), so one wave's softmax overlaps the other's matrix products
+  const bool late = wave >= 4;
   const int c = cg * kWaves + wave;
   const bool active = c < nchunks;
   const int h = g * G + (active ? c % G : 0);
   const int qi = (active ? c / G : 0) * 32 + col;  // query index inside the sample
   const bool qvalid = active && qi < N;
 
-  SampleView sv;
-  sv.k_pre = k_pre; sv.v_pre = v_pre; sv.k_img = k_img; sv.v_img = v_img;
-  sv.p0 = pa; sv.i0 = qa; sv.P = P; sv.Lk = P + N; sv.Hkv = Hkv; sv.g = g;
+  Segments S;
+  S.row_bytes = (int64_t)Hkv * kHeadDim * 2;
+  S.kbase[0] = reinterpret_cast<const uint8_t*>(k_pre + (pa * Hkv + g) * kHeadDim);
+  S.vbase[0] = reinterpret_cast<const uint8_t*>(v_pre + (pa * Hkv + g) * kHeadDim);
+  S.kbase[1] = reinterpret_cast<const uint8_t*>(k_img + (qa * Hkv + g) * kHeadDim);
+  S.vbase[1] = reinterpret_cast<const uint8_t*>(v_img + (qa * Hkv + g) * kHeadDim);
+  S.len[0] = P;
+  S.len[1] = N;
+  S.ntiles[0] = (P + kBN - 1) / kBN;
+  S.ntiles[1] = (N + kBN - 1) / kBN;
+  const int ntiles = S.ntiles[0] + S.ntiles[1];
+
+  // staging offsets: global (inside a tile) and LDS (inside a K or V tile)
+  int goff[2], soff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int qc = tid + kThreads * i;
+    const int row = qc >> 4, chunk = qc & 15;
+    goff[i] = row * (int)S.row_bytes + chunk * 16;
+    soff[i] = row * kRowBytes + ((chunk ^ swz(row)) << 4);
+  }
+
+  // K-fragment reads (A operand of S^T = K Q^T): row kb*32 + col, chunk 2*st + hl.  The
+  // swizzle depends on row % 16 only, so kb adds the constant 32 rows (immediate offset).
+  const int j16 = lane & 15, grp = (lane >> 4) & 1;
+  int kofs[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) kofs[st] = col * kRowBytes + (((2 * st + hl) ^ swz(col)) << 4);
+  // V-fragment reads (A operand of O^T = V^T P^T, transposed): within each 16-lane group,
+  // lane j addresses row key0 + j/4 at dims dim0 + 4*(j%4) and receives dim dim0 + j of
+  // rows key0 .. key0+3.  For step u, read r and dim block db: key0 = 32*(u/2) + 16*(u%2)
+  // + 8*r + 4*hl, dim0 = 32*db + 16*grp.  The u part is a multiple of 16 rows (immediate).
+  int vofs[2][4];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int row = 8 * r + 4 * hl + (j16 >> 2);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int chunk = 4 * db + 2 * grp + ((j16 & 3) >> 1);
+      vofs[r][db] = row * kRowBytes + ((chunk ^ swz(row)) << 4) + ((j16 & 1) << 3);
+    }
+  }
 
   // this lane's slice of Q^T: query qi, dims 16*s + 8*hl .. +7 for k-step s
   bf16x8 qf[8];
@@ -183,96 +217,126 @@ __global__ __launch_bounds__(kThreads, 2) void gen_attn_bf16_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   float m = -INFINITY, lsum = 0.0f;
+  bf16x8 pb[4];  // P of the current tile (late waves: of the previous tile)
 
-  const int Lk = sv.Lk;
-  const int ntiles = (Lk + kBN - 1) / kBN;
-  TileRegs R;
-  load_tile(R, sv, 0, tid);
-  store_tile(smem, R, tid);
-  __syncthreads();
+  Stage R;
+  auto load_stage = [&](int it) {
+    __amdgpu_buffer_rsrc_t rk, rv;
+    tile_rsrc(S, it, rk, rv);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      R.k[i] = buf_load16(rk, goff[i]);
+      R.v[i] = buf_load16(rv, goff[i]);
+    }
+  };
+  auto store_stage = [&](int it) {
+    uint8_t* base = smem + (it % kStages) * kStageBytes;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      *reinterpret_cast<uint4*>(base + soff[i]) = R.k[i];
+      *reinterpret_cast<uint4*>(base + kTileBytes + soff[i]) = R.v[i];
+    }
+  };
 
-  for (int it = 0; it < ntiles; ++it) {
-    const uint16_t* Ks = smem + (it & 1) * kStage;
-    const uint16_t* VT = Ks + kKTile;
-    const bool more = it + 1 < ntiles;
-    if (more) load_tile(R, sv, it + 1, tid);
-
-    if (active) {
-      f32x16 s[2];
+  // scores for tile it, masking, online-softmax update, P in bf16
+  auto qk_softmax = [&](int it) {
+    const uint8_t* Ks = smem + (it % kStages) * kStageBytes;
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-        const uint16_t* krow = Ks + (kb * 32 + col) * kKS + 8 * hl;
-#pragma unroll
-        for (int st = 0; st < 8; ++st) {
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(krow + 16 * st));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb], 0, 0, 0);
-        }
+        const bf16x8 a = as_bf16x8(
+            *reinterpret_cast<const uint4*>(Ks + kofs[st] + kb * 32 * kRowBytes));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb], 0, 0, 0);
       }
-      // keys past the end of the sample (last tile only)
-      if ((it + 1) * kBN > Lk) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = it * kBN + kb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-            if (key >= Lk) s[kb][r] = -INFINITY;
-          }
-      }
-      float mx = s[0][0];
+    const int nvalid = tile_valid(S, it);
+    if (nvalid < kBN) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mx2 = mx * scale_log2;
-      const bool need = mx2 > m + kTau;
-      if (__ballot(need) != 0) {
-        const float mnew = need ? mx2 : m;
-        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-        lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-        m = mnew;
-      }
-      // P in bf16; the row sum adds the same rounded weights (v_dot2 against (1, 1)),
-      // so the normalised weights sum to one exactly and a near one-hot softmax
-      // returns the dominant value without the weight's rounding error
-      bf16x8 pb[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        uint32_t pk[4];
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[u >> 1][(u & 1) * 8 + e], scale_log2, -m));
-          const float p1 =
-              __builtin_amdgcn_exp2f(fmaf(s[u >> 1][(u & 1) * 8 + e + 1], scale_log2, -m));
-          pk[e >> 1] = pack_bf16x2(p0, p1);
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e >> 1]), kOnes2,
-                                                 lsum, false);
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+          if (key >= nvalid) s[kb][r] = -INFINITY;
         }
-        pb[u] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mx2 = mx * scale_log2;
+    const bool need = mx2 > m + kTau;
+    if (__ballot(need) != 0) {
+      const float mnew = need ? mx2 : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      m = mnew;
+    }
+    // the row sum adds the same bf16-rounded weights the PV product uses (v_dot2
+    // against (1, 1)), so the normalised weights sum to one exactly
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t pk[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[u >> 1][(u & 1) * 8 + e], scale_log2, -m));
+        const float p1 =
+            __builtin_amdgcn_exp2f(fmaf(s[u >> 1][(u & 1) * 8 + e + 1], scale_log2, -m));
+        pk[e >> 1] = pack_bf16x2(p0, p1);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e >> 1]), kOnes2,
+                                               lsum, false);
       }
-      // O^T += V^T P^T: k-slot (hl, e) of step u is key 32*(u/2) + 16*(u%2) + 4*hl + 8*(e/4) + e%4
+      pb[u] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    }
+  };
+
+  // O^T += V^T P^T for tile it: k-slot (hl, e) of step u is key
+  // 32*(u/2) + 16*(u%2) + 4*hl + 8*(e/4) + e%4; four independent chains, interleaved
+  auto pv = [&](int it) {
+    const uint8_t* Vs = smem + (it % kStages) * kStageBytes + kTileBytes;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const uint16_t* vrow = VT + (db * 32 + col) * kVS + 4 * hl;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int kbase = 32 * (u >> 1) + 16 * (u & 1);
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kbase);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + kbase + 8);
-          const bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[u], o[db], 0, 0, 0);
-        }
+        const uint8_t* vu = Vs + (32 * (u >> 1) + 16 * (u & 1)) * kRowBytes;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vu + vofs[0][db]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vu + vofs[1][db]));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        const bf16x8 a = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[u], o[db], 0, 0, 0);
+      }
+  };
+
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const bool more = it + 1 < ntiles;
+    if (more) load_stage(it + 1);
+    if (active) {
+      if (late) {
+        if (it > 0) pv(it - 1);
+        qk_softmax(it);
+      } else {
+        qk_softmax(it);
+        pv(it);
       }
     }
-    if (more) store_tile(smem + ((it + 1) & 1) * kStage, R, tid);
+    if (more) store_stage(it + 1);
     __syncthreads();
   }
+  if (active && late) pv(ntiles - 1);
 
   const float ltot = lsum + __shfl_xor(lsum, 32);
   if (qvalid) {
@@ -295,8 +359,9 @@ __global__ __launch_bounds__(kThreads, 2) void gen_attn_bf16_kernel(
 // fp32 path
 // ---------------------------------------------------------------------------------------
 constexpr int kF32Keys = 32;
+constexpr int kF32Threads = 256;
 
-__global__ __launch_bounds__(kThreads) void gen_attn_f32_kernel(
+__global__ __launch_bounds__(kF32Threads) void gen_attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k_img, const float* __restrict__ v_img,
     const float* __restrict__ k_pre, const float* __restrict__ v_pre,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_p, int Hq, int Hkv,
@@ -320,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void gen_attn_f32_kernel(
   const int P = (int)((pb_ - pa) < max_p ? (pb_ - pa) : max_p);
   const int G = Hq / Hkv;
   const int rows = N * G;
-  const int rows_per_block = kThreads / 2;
+  const int rows_per_block = kF32Threads / 2;
   if (rb * rows_per_block >= rows) return;
 
   const int tid = threadIdx.x;
@@ -340,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void gen_attn_f32_kernel(
   float m = -INFINITY, l = 0.0f;
   const int Lk = P + N;
   for (int k0 = 0; k0 < Lk; k0 += kF32Keys) {
-    for (int e = tid; e < kF32Keys * kHeadDim; e += kThreads) {
+    for (int e = tid; e < kF32Keys * kHeadDim; e += kF32Threads) {
       const int j = k0 + e / kHeadDim, d = e % kHeadDim;
       float kv = 0.0f, vv = 0.0f;
       if (j < P) {
@@ -418,9 +483,9 @@ hipError_t launch_gen_attn_f32(const float* q, const float* k_img, const float* 
   if (max_q == 0 || Tq == 0) return hipSuccess;
   const int G = Hq / Hkv;
   const int64_t rows = (int64_t)max_q * G;
-  const int64_t n_rb = (rows + kThreads / 2 - 1) / (kThreads / 2);
+  const int64_t n_rb = (rows + kF32Threads / 2 - 1) / (kF32Threads / 2);
   const int64_t blocks = n_rb * Hkv * B;
-  hipLaunchKernelGGL(gen_attn_f32_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, q,
+  hipLaunchKernelGGL(gen_attn_f32_kernel, dim3((unsigned)blocks), dim3(kF32Threads), 0, stream, q,
                      k_img, v_img, k_pre, v_pre, cu_q, cu_p, Hq, Hkv, (int)n_rb, max_q, max_p, Tq,
                      Tp, scale, out, lse);
   return hipGetLastError();
