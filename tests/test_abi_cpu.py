@@ -1,0 +1,152 @@
+"""The C-ABI library on the CPU: it loads, exports every call include/neo.h declares,
+and rejects invalid arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import pixel_space_flow_amd as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "neo.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(neo_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(P.LIB_PATH):
+        import pixel_space_flow_amd.build as b
+        b.build()
+    return P.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert set(names) == set(P.EXPORTED_SYMBOLS), names
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+
+
+def test_status_strings(L):
+    for code, text in enumerate(["ok", "null pointer", "bad shape", "bad value", "unsupported",
+                                 "HIP error"]):
+        assert L.neo_status_string(code).decode() == text
+    assert L.neo_status_string(99).decode() == "unknown status"
+
+
+# a fake, 256-aligned "device" address: never dereferenced, because every call below
+# fails validation before any HIP call
+FAKE = 1 << 40
+W = FAKE + 4096
+
+
+def _rope(L, **kw):
+    a = dict(q_in=FAKE, k_in=FAKE + (1 << 30), q_out=FAKE + (2 << 30), k_out=FAKE + (3 << 30),
+             T=16, Hq=4, Hkv=1, D=128, w0=W, w1=W, w2=W, w3=W, pos=W, th=5e6, thw=1e4, eps=1e-6,
+             dtype=P.NEO_BF16)
+    a.update(kw)
+    return L.neo_qknorm_rope3(a["q_in"], a["k_in"], a["q_out"], a["k_out"], a["T"], a["Hq"],
+                              a["Hkv"], a["D"], a["w0"], a["w1"], a["w2"], a["w3"], a["pos"],
+                              a["th"], a["thw"], a["eps"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), P.NEO_ERR_UNSUPPORTED),
+    (dict(D=64), P.NEO_ERR_SHAPE),
+    (dict(Hq=0), P.NEO_ERR_SHAPE),
+    (dict(T=-1), P.NEO_ERR_SHAPE),
+    (dict(th=0.0), P.NEO_ERR_VALUE),
+    (dict(thw=math.inf), P.NEO_ERR_VALUE),
+    (dict(eps=-1.0), P.NEO_ERR_VALUE),
+    (dict(eps=math.nan), P.NEO_ERR_VALUE),
+    (dict(q_in=None), P.NEO_ERR_NULL),
+    (dict(pos=None), P.NEO_ERR_NULL),
+    (dict(q_in=FAKE + 8), P.NEO_ERR_VALUE),                    # misaligned
+    (dict(q_out=FAKE + 512), P.NEO_ERR_VALUE),                 # partial overlap with q_in
+    (dict(k_out=FAKE + 256), P.NEO_ERR_VALUE),                 # k_out overlaps q_in
+])
+def test_rope_validation(L, kw, status):
+    assert _rope(L, **kw) == status
+    assert L.neo_last_error().decode().startswith("neo_qknorm_rope3")
+
+
+def test_rope_empty_is_ok(L):
+    assert _rope(L, T=0, q_in=None, k_in=None, q_out=None, k_out=None) == P.NEO_OK
+    assert L.neo_last_error().decode() == ""
+
+
+def _attn(L, **kw):
+    a = dict(q=FAKE, ki=FAKE + (1 << 30), vi=FAKE + (2 << 30), kp=FAKE + (3 << 30),
+             vp=FAKE + (4 << 30), cuq=W, cup=W + 256, B=1, Hq=32, Hkv=8, D=128, Tq=4096, Tp=512,
+             mq=4096, mp=512, scale=0.0, out=FAKE + (5 << 30), lse=None, dtype=P.NEO_BF16)
+    a.update(kw)
+    return L.neo_gen_attn_fwd(a["q"], a["ki"], a["vi"], a["kp"], a["vp"], a["cuq"], a["cup"],
+                              a["B"], a["Hq"], a["Hkv"], a["D"], a["Tq"], a["Tp"], a["mq"],
+                              a["mp"], a["scale"], a["out"], a["lse"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), P.NEO_ERR_UNSUPPORTED),
+    (dict(D=256), P.NEO_ERR_SHAPE),
+    (dict(B=0), P.NEO_ERR_SHAPE),
+    (dict(Hkv=7), P.NEO_ERR_SHAPE),                            # Hq % Hkv != 0
+    (dict(mq=-1), P.NEO_ERR_SHAPE),
+    (dict(mq=5000), P.NEO_ERR_SHAPE),                          # above the tensor's rows
+    (dict(Tq=-5), P.NEO_ERR_SHAPE),
+    (dict(scale=math.inf), P.NEO_ERR_VALUE),
+    (dict(q=None), P.NEO_ERR_NULL),
+    (dict(cuq=None), P.NEO_ERR_NULL),
+    (dict(kp=None), P.NEO_ERR_NULL),                           # prefix rows but no pointer
+    (dict(out=FAKE + (1 << 30)), P.NEO_ERR_VALUE),             # out aliases k_img
+    (dict(lse=FAKE + (5 << 30)), P.NEO_ERR_VALUE),             # lse overlaps out
+    (dict(vi=FAKE + (2 << 30) + 4), P.NEO_ERR_VALUE),          # misaligned
+    (dict(B=1 << 30, Hkv=8, mq=4096), P.NEO_ERR_SHAPE),        # grid beyond 2^31 workgroups
+])
+def test_attn_validation(L, kw, status):
+    assert _attn(L, **kw) == status
+    assert L.neo_last_error().decode().startswith("neo_gen_attn_fwd")
+
+
+def test_attn_empty_is_ok(L):
+    assert _attn(L, mq=0, q=None) == P.NEO_OK
+    assert _attn(L, Tq=0, mq=0) == P.NEO_OK
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE + 4096, -1, 0.1, 0.2, 0.02), P.NEO_ERR_SHAPE),
+    ((FAKE, FAKE + 4096, 10, 0.3, 0.2, 0.02), P.NEO_ERR_VALUE),    # t_next < t
+    ((FAKE, FAKE + 4096, 10, 0.1, 0.2, 0.0), P.NEO_ERR_VALUE),     # t_eps <= 0
+    ((FAKE, FAKE + 4096, 10, math.nan, 0.2, 0.02), P.NEO_ERR_VALUE),
+    ((None, FAKE, 10, 0.1, 0.2, 0.02), P.NEO_ERR_NULL),
+    ((FAKE, FAKE + 8, 10, 0.1, 0.2, 0.02), P.NEO_ERR_VALUE),       # partial overlap
+    ((FAKE + 2, FAKE + 4096, 10, 0.1, 0.2, 0.02), P.NEO_ERR_VALUE),  # misaligned
+])
+def test_euler_validation(L, args, status):
+    assert L.neo_fm_euler_step(*args, None) == status
+    assert L.neo_last_error().decode().startswith("neo_fm_euler_step")
+
+
+def test_euler_empty_is_ok(L):
+    assert L.neo_fm_euler_step(None, None, 0, 0.1, 0.2, 0.02, None) == P.NEO_OK
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros((4, 4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="HIP device"):
+        P.gen_attn_fwd(q, q[:, :1], q[:, :1], q[:0, :1], q[:0, :1], torch.zeros(2, dtype=torch.int32),
+                       torch.zeros(2, dtype=torch.int32), 4, 0)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(P, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(P, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        P.lib()
