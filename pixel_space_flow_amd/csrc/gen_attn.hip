@@ -59,9 +59,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kBN = 64;                      // keys per tile
 constexpr int kRowBytes = kHeadDim * 2;      // one K or V row in LDS (no padding)
 constexpr int kTileBytes = kBN * kRowBytes;  // 16 KB
-constexpr int kStageBytes = 2 * kTileBytes;  // K tile + V tile
-constexpr int kStages = 3;
-constexpr float kTau = 8.0f;                 // lazy-rescale threshold (log2 units)
+constexpr float kTwoTau = 256.0f;            // bound on any softmax weight (2^8)
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 constexpr int kBufFlags = 0x00020000;        // raw buffer, 32-bit data format (gfx9 family)
 
@@ -111,11 +109,16 @@ __device__ __forceinline__ int tile_valid(const Segments& S, int it) {
   return S.len[seg] - tl * kBN;
 }
 
-// Staging: thread t moves 16-byte chunks q = t and t + 512 of the K tile and of the V tile
+// Staging: thread t moves 16-byte chunks q = t and t + 512 of one K tile and one V tile
 // (row q / 16, chunk q % 16) from HBM to registers, then to their swizzled LDS slots.
 struct Stage {
   uint4 k[2], v[2];
 };
+
+// LDS: two K tiles and two V tiles.  Iteration t computes tile t's scores (K buffer
+// t % 2) and tile t-1's PV product (V buffer (t-1) % 2) while tile t+1's K and tile t's
+// V are staged into the other buffers.
+constexpr int kLdsBytes = 4 * kTileBytes;  // 64 KB
 
 __global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_img,
@@ -124,7 +127,7 @@ __global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
     const int32_t* __restrict__ cu_p, int Hq, int Hkv, int n_cg, int max_q, int max_p,
     int64_t Tq, int64_t Tp, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
 
   const uint32_t id = xcd_remap(blockIdx.x, gridDim.x);
   const int cg = (int)(id % (uint32_t)n_cg);
@@ -148,9 +151,6 @@ __global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, col = lane & 31;
-  // waves w and w + 4 share a SIMD; the upper four run half a tile behind (PV of the
-  // previous tile first), so one wave's softmax overlaps the other's matrix products
-  const bool late = wave >= 4;
   const int c = cg * kWaves + wave;
   const bool active = c < nchunks;
   const int h = g * G + (active ? c % G : 0);
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
   S.ntiles[1] = (N + kBN - 1) / kBN;
   const int ntiles = S.ntiles[0] + S.ntiles[1];
 
-  // staging offsets: global (inside a tile) and LDS (inside a K or V tile)
+  // staging offsets: global (inside a tile) and LDS (inside a tile)
   int goff[2], soff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -216,64 +216,117 @@ __global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+  // m: reference maximum (log2 units); every weight exp2(s*c - m) is kept <= 2^8
   float m = -INFINITY, lsum = 0.0f;
-  bf16x8 pb[4];  // P of the current tile (late waves: of the previous tile)
 
   Stage R;
-  auto load_stage = [&](int it) {
+  auto load_k = [&](int t) {
     __amdgpu_buffer_rsrc_t rk, rv;
-    tile_rsrc(S, it, rk, rv);
+    tile_rsrc(S, t, rk, rv);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      R.k[i] = buf_load16(rk, goff[i]);
-      R.v[i] = buf_load16(rv, goff[i]);
-    }
+    for (int i = 0; i < 2; ++i) R.k[i] = buf_load16(rk, goff[i]);
   };
-  auto store_stage = [&](int it) {
-    uint8_t* base = smem + (it % kStages) * kStageBytes;
+  auto load_v = [&](int t) {
+    __amdgpu_buffer_rsrc_t rk, rv;
+    tile_rsrc(S, t, rk, rv);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *reinterpret_cast<uint4*>(base + soff[i]) = R.k[i];
-      *reinterpret_cast<uint4*>(base + kTileBytes + soff[i]) = R.v[i];
-    }
+    for (int i = 0; i < 2; ++i) R.v[i] = buf_load16(rv, goff[i]);
+  };
+  auto store_k = [&](uint8_t* base) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(base + soff[i]) = R.k[i];
+  };
+  auto store_v = [&](uint8_t* base) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(base + soff[i]) = R.v[i];
   };
 
-  // scores for tile it, masking, online-softmax update, P in bf16
-  auto qk_softmax = [&](int it) {
-    const uint8_t* Ks = smem + (it % kStages) * kStageBytes;
-    f32x16 s[2];
+  // scores of one tile from the K tile at Ks (16 MFMAs, two interleaved chains)
+  auto qk = [&](const uint8_t* Ks, f32x16 (&sacc)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
 #pragma unroll
     for (int st = 0; st < 8; ++st)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 a = as_bf16x8(
             *reinterpret_cast<const uint4*>(Ks + kofs[st] + kb * 32 * kRowBytes));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb], 0, 0, 0);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], sacc[kb], 0, 0, 0);
       }
-    const int nvalid = tile_valid(S, it);
+  };
+
+  // keys past the end of the segment (its last tile only) score -inf
+  auto mask = [&](int t, f32x16 (&sacc)[2]) {
+    const int nvalid = tile_valid(S, t);
     if (nvalid < kBN) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-          if (key >= nvalid) s[kb][r] = -INFINITY;
+          if (key >= nvalid) sacc[kb][r] = -INFINITY;
         }
     }
-    float mx = s[0][0];
+  };
+
+  // P = exp2(s*c - m) in bf16 and the row sum of the same rounded weights (v_dot2 against
+  // (1, 1)), so the normalised weights sum to one exactly.  Returns this tile's sum.
+  auto exp_tile = [&](const f32x16 (&sacc)[2], bf16x8 (&pw)[4]) -> float {
+    float tsum = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int u = 0; u < 4; ++u) {
+      uint32_t pk[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mx2 = mx * scale_log2;
-    const bool need = mx2 > m + kTau;
-    if (__ballot(need) != 0) {
-      const float mnew = need ? mx2 : m;
+      for (int e = 0; e < 8; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[u >> 1][(u & 1) * 8 + e], scale_log2, -m));
+        const float p1 =
+            __builtin_amdgcn_exp2f(fmaf(sacc[u >> 1][(u & 1) * 8 + e + 1], scale_log2, -m));
+        pk[e >> 1] = pack_bf16x2(p0, p1);
+        tsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e >> 1]), kOnes2,
+                                               tsum, false);
+      }
+      pw[u] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    }
+    return tsum;
+  };
+
+  // O^T += V^T P^T from the V tile at Vs (16 MFMAs, four chains).  k-slot (hl, e) of
+  // step u is key 32*(u/2) + 16*(u%2) + 4*hl + 8*(e/4) + e%4.
+  auto pv = [&](const uint8_t* Vs, const bf16x8 (&pw)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint8_t* vu = Vs + (32 * (u >> 1) + 16 * (u & 1)) * kRowBytes;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vu + vofs[0][db]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vu + vofs[1][db]));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        const bf16x8 av = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pw[u], o[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // Softmax weights of the current tile, with the previous tile's PV product issued
+  // first so the exponentials run in its shadow.  The common path uses the running
+  // reference m as is: if this tile's sum of rounded weights stays <= 2^8 on every
+  // lane, no weight exceeds 2^8 and nothing else is needed.  Otherwise (the first tile,
+  // or a new larger score), the true maximum is taken, O and l are rescaled -- after
+  // the previous PV product, which used the old m -- and the weights are recomputed.
+  auto softmax_pv = [&](const f32x16 (&sacc)[2], bf16x8 (&pw)[4], const uint8_t* Vprev,
+                        const bf16x8 (&pprev)[4], bool have_prev) {
+    if (have_prev) pv(Vprev, pprev);
+    float tsum = exp_tile(sacc, pw);
+    if (__ballot(!(tsum <= kTwoTau)) != 0) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m, mx * scale_log2);
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);
       lsum *= alpha;
 #pragma unroll
@@ -281,62 +334,52 @@ __global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       m = mnew;
+      tsum = exp_tile(sacc, pw);
     }
-    // the row sum adds the same bf16-rounded weights the PV product uses (v_dot2
-    // against (1, 1)), so the normalised weights sum to one exactly
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      uint32_t pk[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[u >> 1][(u & 1) * 8 + e], scale_log2, -m));
-        const float p1 =
-            __builtin_amdgcn_exp2f(fmaf(s[u >> 1][(u & 1) * 8 + e + 1], scale_log2, -m));
-        pk[e >> 1] = pack_bf16x2(p0, p1);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e >> 1]), kOnes2,
-                                               lsum, false);
-      }
-      pb[u] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
-    }
+    lsum += tsum;
   };
 
-  // O^T += V^T P^T for tile it: k-slot (hl, e) of step u is key
-  // 32*(u/2) + 16*(u%2) + 4*hl + 8*(e/4) + e%4; four independent chains, interleaved
-  auto pv = [&](int it) {
-    const uint8_t* Vs = smem + (it % kStages) * kStageBytes + kTileBytes;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint8_t* vu = Vs + (32 * (u >> 1) + 16 * (u & 1)) * kRowBytes;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vu + vofs[0][db]));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vu + vofs[1][db]));
-        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-        const bf16x8 a = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[u], o[db], 0, 0, 0);
-      }
-  };
+  uint8_t* const kb0 = smem;
+  uint8_t* const kb1 = smem + kTileBytes;
+  uint8_t* const vb0 = smem + 2 * kTileBytes;
+  uint8_t* const vb1 = smem + 3 * kTileBytes;
 
-  load_stage(0);
-  store_stage(0);
+  // prologue: K(0) in LDS
+  load_k(0);
+  store_k(kb0);
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
-    const bool more = it + 1 < ntiles;
-    if (more) load_stage(it + 1);
+  f32x16 sacc[2];
+  bf16x8 pa_[4], pb2[4];  // P of even / odd tiles
+
+  // iteration t: stage K(t+1), V(t); scores of tile t; PV of tile t-1 with tile t's
+  // softmax.  Kcur/Knext and Vprev/Vcur alternate with the parity of t.
+  auto iteration = [&](int t, const uint8_t* Kcur, uint8_t* Knext, const uint8_t* Vprev,
+                       uint8_t* Vcur, bf16x8 (&pcur)[4], const bf16x8 (&pprev)[4]) {
+    const bool kmore = t + 1 < ntiles;
+    if (kmore) load_k(t + 1);
+    load_v(t);
     if (active) {
-      if (late) {
-        if (it > 0) pv(it - 1);
-        qk_softmax(it);
-      } else {
-        qk_softmax(it);
-        pv(it);
-      }
+      qk(Kcur, sacc);
+      mask(t, sacc);
+      softmax_pv(sacc, pcur, Vprev, pprev, t > 0);
     }
-    if (more) store_stage(it + 1);
+    if (kmore) store_k(Knext);
+    store_v(Vcur);
     __syncthreads();
+  };
+
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    iteration(t, kb0, kb1, vb1, vb0, pa_, pb2);
+    iteration(t + 1, kb1, kb0, vb0, vb1, pb2, pa_);
   }
-  if (active && late) pv(ntiles - 1);
+  if (t < ntiles) {
+    iteration(t, kb0, kb1, vb1, vb0, pa_, pb2);
+    if (active) pv(vb0, pa_);
+  } else if (active) {
+    pv(vb1, pb2);
+  }
 
   const float ltot = lsum + __shfl_xor(lsum, 32);
   if (qvalid) {
