@@ -122,7 +122,9 @@ neo_status neo_qknorm_rope3(const void *q_in, const void *k_in, void *q_out, voi
  *   max_seqlen_q, max_seqlen_prefix: host-side upper bounds of the per-sample
  *     lengths (no device-to-host copy is made); they size the launch grid and
  *     must not be below the true maxima (a precondition, as in varlen flash
- *     attention: rows and keys beyond the bound are not computed).
+ *     attention: rows and keys beyond the bound are not computed).  One
+ *     sample's K or V rows must span less than 2 GiB (max_seqlen * Hkv * 256 B
+ *     for bf16, checked at the fp32 size).
  *   softmax_scale: <= 0 selects 1/sqrt(head_dim); otherwise finite.
  *   out      [Tq, Hq, 128] dtype, device: written.  Must not overlap inputs.
  *   lse      [Hq, Tq] fp32, device, natural log, or NULL to skip.

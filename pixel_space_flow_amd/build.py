@@ -35,7 +35,7 @@ FLAGS = [
 
 def _compile(src: str, asm: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *os.environ.get("NEO_HIPCC_EXTRA", "").split(), "-c", src, "-o", obj]
     if asm:
         cmd += ["-save-temps=obj"]
     r = subprocess.run(cmd, capture_output=True, text=True)

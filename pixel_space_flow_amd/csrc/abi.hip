@@ -125,6 +125,10 @@ neo_status neo_gen_attn_fwd(const void* q, const void* k_img, const void* v_img,
                 (long long)total_q, (long long)total_prefix);
   if (max_seqlen_q > total_q || max_seqlen_prefix > total_prefix)
     return fail(NEO_ERR_SHAPE, "neo_gen_attn_fwd: max_seqlen exceeds the tensor's rows");
+  // one sample's K or V segment is addressed with 32-bit byte offsets
+  if ((int64_t)max_seqlen_q * Hkv * NEO_HEAD_DIM * 4 >= ((int64_t)1 << 31) ||
+      (int64_t)max_seqlen_prefix * Hkv * NEO_HEAD_DIM * 4 >= ((int64_t)1 << 31))
+    return fail(NEO_ERR_SHAPE, "neo_gen_attn_fwd: one sample's K/V rows exceed 2 GiB");
   if (!isfinite(softmax_scale))
     return fail(NEO_ERR_VALUE, "neo_gen_attn_fwd: softmax_scale must be finite");
   // grid size: one workgroup per (sample, KV head, 8 chunks of 32 query rows), or per

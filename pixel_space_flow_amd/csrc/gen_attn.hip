@@ -69,7 +69,7 @@ constexpr int kBufFlags = 0x00020000;        // raw buffer, 32-bit data format (
 // and the transposed V reads (4 consecutive rows, 4 consecutive chunks per half-wave).
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t nbytes) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
                                            kBufFlags);
 }
@@ -86,7 +86,9 @@ struct Segments {
   const uint8_t* vbase[2];
   int len[2];
   int ntiles[2];
-  int64_t row_bytes;  // Hkv * 128 * 2
+  int64_t row_bytes;    // Hkv * 128 * 2
+  uint32_t row_bytes32;
+  uint32_t tile_bytes;  // 64 rows
 };
 
 // One tile = 64 consecutive rows of one key segment.  The buffer resource starts at the
@@ -94,13 +96,14 @@ struct Segments {
 // zeros for rows past the segment: no branches and no per-row address arithmetic.
 __device__ __forceinline__ void tile_rsrc(const Segments& S, int it, __amdgpu_buffer_rsrc_t& rk,
                                           __amdgpu_buffer_rsrc_t& rv) {
-  const int seg = it < S.ntiles[0] ? 0 : 1;
-  const int tl = seg == 0 ? it : it - S.ntiles[0];
-  const int64_t off = (int64_t)tl * kBN * S.row_bytes;
-  const int rows = S.len[seg] - tl * kBN;
-  const int64_t nbytes = (int64_t)(rows < kBN ? rows : kBN) * S.row_bytes;  // < 2^32
-  rk = make_rsrc(S.kbase[seg] + off, nbytes);
-  rv = make_rsrc(S.vbase[seg] + off, nbytes);
+  const bool pre = it < S.ntiles[0];
+  const int tl = pre ? it : it - S.ntiles[0];
+  const int rows = (pre ? S.len[0] : S.len[1]) - tl * kBN;
+  // one sample's segment spans < 2^31 bytes (checked by the caller), so 32-bit offsets
+  const uint32_t off = (uint32_t)tl * S.tile_bytes;
+  const uint32_t nbytes = (uint32_t)(rows < kBN ? rows : kBN) * S.row_bytes32;
+  rk = make_rsrc((pre ? S.kbase[0] : S.kbase[1]) + off, nbytes);
+  rv = make_rsrc((pre ? S.vbase[0] : S.vbase[1]) + off, nbytes);
 }
 
 __device__ __forceinline__ int tile_valid(const Segments& S, int it) {
@@ -159,6 +162,8 @@ __global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
 
   Segments S;
   S.row_bytes = (int64_t)Hkv * kHeadDim * 2;
+  S.row_bytes32 = (uint32_t)S.row_bytes;
+  S.tile_bytes = (uint32_t)S.row_bytes * kBN;
   S.kbase[0] = reinterpret_cast<const uint8_t*>(k_pre + (pa * Hkv + g) * kHeadDim);
   S.vbase[0] = reinterpret_cast<const uint8_t*>(v_pre + (pa * Hkv + g) * kHeadDim);
   S.kbase[1] = reinterpret_cast<const uint8_t*>(k_img + (qa * Hkv + g) * kHeadDim);

@@ -108,6 +108,7 @@ def _attn(L, **kw):
     (dict(lse=FAKE + (5 << 30)), P.NEO_ERR_VALUE),             # lse overlaps out
     (dict(vi=FAKE + (2 << 30) + 4), P.NEO_ERR_VALUE),          # misaligned
     (dict(B=1 << 30, Hkv=8, mq=4096), P.NEO_ERR_SHAPE),        # grid beyond 2^31 workgroups
+    (dict(Tq=1 << 21, mq=1 << 21), P.NEO_ERR_SHAPE),            # one sample's K/V beyond 2 GiB
 ])
 def test_attn_validation(L, kw, status):
     assert _attn(L, **kw) == status
