@@ -44,7 +44,56 @@ def parse():
                     help="query tokens in the oracle's attention sample")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters, if present")
+    ap.add_argument("--calib-mib", type=int, default=256,
+                    help="size of the device-to-device copy run once before warm-up, the known-size "
+                         "reference for the HBM byte counters")
+    ap.add_argument("--derive-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
+                         "WRITE_SIZE, -f csv) into HBM bytes per launch and write --traffic-json")
     return ap.parse_args()
+
+
+KERNELS = {"gen_attn_bf16_kernel": "gen_attn_bf16_kernel", "qknorm_rope3": "qknorm_rope3_kernel",
+           "fm_euler_step": "euler_vec4_kernel"}
+
+
+def _counter_rows(d, counter):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
+    return rows
+
+
+def derive_traffic(a):
+    """HBM bytes per launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by
+    what the same counter reads for the known-size calibration copy."""
+    out = {"calibration_bytes": a.calib_mib << 20, "workload": a.workload}
+    for counter, d in (("FETCH_SIZE", a.derive_traffic[0]), ("WRITE_SIZE", a.derive_traffic[1])):
+        rows = _counter_rows(d, counter)
+        calib_bytes = a.calib_mib << 20
+        copies = [float(r["Counter_Value"]) * 1024 for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        big = [c for c in copies if c > 0.5 * calib_bytes]
+        if not big:
+            raise SystemExit(f"{counter}: calibration copy not found in {d}")
+        scale = calib_bytes / (sum(big) / len(big))
+        out[f"{counter}_scale"] = scale
+        for key, pat in KERNELS.items():
+            vals = [float(r["Counter_Value"]) * 1024 for r in rows if pat in r["Kernel_Name"]]
+            if vals:
+                out.setdefault(key, {})[counter] = sum(vals) / len(vals) * scale
+    for key in KERNELS:
+        if key in out and {"FETCH_SIZE", "WRITE_SIZE"} <= set(out[key]):
+            out[key]["bytes"] = out[key]["FETCH_SIZE"] + out[key]["WRITE_SIZE"]
+    os.makedirs(os.path.dirname(a.traffic_json), exist_ok=True)
+    with open(a.traffic_json, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def algorithmic(w):
@@ -85,6 +134,9 @@ def cpu_baseline(w, kp, vp, n_tokens):
 
 def main():
     a = parse()
+    if a.derive_traffic:
+        derive_traffic(a)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -131,6 +183,15 @@ def main():
     max_q, max_p = max(w.n_img), max(w.n_prefix)
     t, tn = w.t_grid[0], w.t_grid[1]
 
+    # known-size plain copy: the reference the HBM byte counters are scaled by
+    if a.calib_mib > 0:
+        src = torch.empty(a.calib_mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     def step(i, ev=None):
         s = sets[i % len(sets)]
         if ev is not None:
@@ -172,7 +233,8 @@ def main():
     if os.path.exists(a.traffic_json):
         with open(a.traffic_json) as f:
             tj = json.load(f)
-        traffic = tj.get("gen_attn_bf16_kernel", {}).get(a.workload)
+        if tj.get("workload") == a.workload:
+            traffic = tj.get("gen_attn_bf16_kernel", {}).get("bytes")
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic}
     pro_gbs = pro_bytes / (float(pro_ms.mean()) * 1e-3) / 1e9
