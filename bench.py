@@ -55,6 +55,8 @@ def parse():
 
 KERNELS = {"gen_attn_bf16_kernel": "gen_attn_bf16_kernel", "qknorm_rope3": "qknorm_rope3_kernel",
            "fm_euler_step": "euler_vec4_kernel"}
+KERNEL_SOURCES = {"gen_attn_bf16_kernel": "gen_attn.hip", "qknorm_rope3": "qknorm_rope3.hip",
+                  "fm_euler_step": "euler_step.hip"}
 
 
 def _counter_rows(d, counter):
@@ -68,6 +70,14 @@ def _counter_rows(d, counter):
         with open(f) as fh:
             rows += [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
     return rows
+
+
+def _kernel_source_hash(key):
+    """sha256 of the HIP source a kernel is built from: byte counts taken from one build
+    are not reported for another."""
+    import hashlib
+    with open(os.path.join(ROOT, "pixel_space_flow_amd", "csrc", KERNEL_SOURCES[key]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
 def derive_traffic(a):
@@ -90,6 +100,7 @@ def derive_traffic(a):
     for key in KERNELS:
         if key in out and {"FETCH_SIZE", "WRITE_SIZE"} <= set(out[key]):
             out[key]["bytes"] = out[key]["FETCH_SIZE"] + out[key]["WRITE_SIZE"]
+            out[key]["source_sha256"] = _kernel_source_hash(key)
     os.makedirs(os.path.dirname(a.traffic_json), exist_ok=True)
     with open(a.traffic_json, "w") as f:
         json.dump(out, f, indent=1)
@@ -233,8 +244,10 @@ def main():
     if os.path.exists(a.traffic_json):
         with open(a.traffic_json) as f:
             tj = json.load(f)
-        if tj.get("workload") == a.workload:
-            traffic = tj.get("gen_attn_bf16_kernel", {}).get("bytes")
+        att = tj.get("gen_attn_bf16_kernel", {})
+        if (tj.get("workload") == a.workload
+                and att.get("source_sha256") == _kernel_source_hash("gen_attn_bf16_kernel")):
+            traffic = att.get("bytes")
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic}
     pro_gbs = pro_bytes / (float(pro_ms.mean()) * 1e-3) / 1e9

@@ -20,21 +20,23 @@
 //     score accumulator to the second MFMA without any data movement.  V stays
 //     row-major in LDS and is read with ds_read_b64_tr_b16, whose 16-lane transpose
 //     hands each lane 4 consecutive keys of one dim;
-//   * LDS rows are XOR-swizzled at 16-byte granularity (no padding), which keeps the
-//     staging writes, the K reads and the transposed V reads free of bank conflicts;
-//   * waves w and w+4 share a SIMD; the upper four run half a tile behind (the PV
-//     product of the previous tile first), so one wave's softmax overlaps the other's
-//     matrix products instead of both waves contending for the same unit at once;
+//   * software pipeline over 32-key sub-tiles: each of the 8 slots of a step issues one
+//     score MFMA of sub-tile s+1, one PV MFMA of sub-tile s-1 and one pair of weights of
+//     sub-tile s, so the exponentials of one sub-tile run under the matrix products of
+//     its neighbours inside every wave; the LDS operands are read three slots ahead;
 //   * online softmax in fp32 on exp2 with the 1/sqrt(d) * log2(e) scale folded into one
 //     FMA; the row sum adds the bf16-rounded weights that the PV product uses.  The
-//     running maximum is raised only when a tile's maximum exceeds it by more than 2^8,
-//     so the O rescale (64 multiplies per lane) runs on the first tile and almost never
-//     afterwards, while every exponent stays <= 2^8; the final O / l is the same
-//     quotient whichever reference maximum was used;
-//   * K/V tiles of 64 keys from raw buffer loads: the resource of each tile ends at its
-//     segment's end, so rows past it read as zeros (their scores are then set to -inf)
-//     with no per-row address arithmetic.  Three LDS stages; the next tile's loads are
-//     in flight during the current tile's math, one barrier per tile;
+//     running maximum is raised only when a sub-tile's sum of weights exceeds 2^8, so
+//     the O rescale (64 multiplies per lane) runs on the first sub-tile and almost never
+//     afterwards, while every weight stays <= 2^8; the final O / l is the same quotient
+//     whichever reference maximum was used;
+//   * K/V tiles of 64 keys go from HBM/L2 straight into LDS (buffer loads with the LDS
+//     destination, no register round trip).  The resource of each tile ends at its
+//     segment's end, so rows past it arrive as zeros (their scores are then set to
+//     -inf) with no per-row address arithmetic.  Three K and three V buffers: the loads
+//     of K tile T+2 and V tile T+1 are in flight during the math of tile T; one barrier
+//     per tile.  LDS rows are XOR-swizzled at 16-byte granularity, which keeps the
+//     K-fragment reads and the transposed V reads free of bank conflicts;
 //   * the workgroup order is remapped so each XCD works on contiguous (sample, KV head)
 //     ranges and its L2 holds that head's K/V.
 //
@@ -43,6 +45,8 @@
 #include "neo_internal.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 namespace neo {
 namespace {
@@ -56,17 +60,22 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kThreads = 512;                // 8 waves, two per SIMD
 constexpr int kWaves = kThreads / 64;
-constexpr int kBN = 64;                      // keys per tile
-constexpr int kRowBytes = kHeadDim * 2;      // one K or V row in LDS (no padding)
-constexpr int kTileBytes = kBN * kRowBytes;  // 16 KB
+constexpr int kBN = 64;                      // keys per LDS tile (one barrier per tile)
+constexpr int kRow = kHeadDim * 2;          // one K or V row in LDS (no padding)
+constexpr int kTileBytes = kBN * kRow;       // 16 KB
 constexpr float kTwoTau = 256.0f;            // bound on any softmax weight (2^8)
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 constexpr int kBufFlags = 0x00020000;        // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kPrefetch = 3;                 // slots of LDS operands read ahead (<= 3)
 
 // LDS tiles hold 64 rows of 16 chunks (16 bytes = 8 dims each).  Chunk c of row r is
-// stored at slot c ^ swz(r), which makes all three access patterns conflict-free:
-// the row-wise 16-byte writes, the K-fragment reads (16 consecutive rows, one chunk)
-// and the transposed V reads (4 consecutive rows, 4 consecutive chunks per half-wave).
+// stored at slot c ^ swz(r), which keeps the K-fragment reads (16 consecutive rows, one
+// chunk) and the transposed V reads (4 consecutive rows, 4 consecutive chunks per
+// half-wave) free of bank conflicts.  Tiles are written by buffer loads that deliver
+// straight into LDS: one such load fills 1 KB (lane L writes bytes 16L .. 16L+15), so
+// the swizzle is applied on the fetch side (lane L fetches the chunk that belongs in its
+// slot).  Three K and three V tiles: in iteration T the waves read K tiles T, T+1 and V
+// tiles T-1, T while K tile T+2 and V tile T+1 are in flight.
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
@@ -86,42 +95,32 @@ struct Segments {
   const uint8_t* vbase[2];
   int len[2];
   int ntiles[2];
-  int64_t row_bytes;    // Hkv * 128 * 2
-  uint32_t row_bytes32;
+  uint32_t row_bytes;   // Hkv * 128 * 2
   uint32_t tile_bytes;  // 64 rows
 };
 
-// One tile = 64 consecutive rows of one key segment.  The buffer resource starts at the
-// tile's first row and ends at the segment's end, so the hardware range check returns
-// zeros for rows past the segment: no branches and no per-row address arithmetic.
+// One LDS tile = 64 consecutive rows of one key segment.  The buffer resource starts at
+// the tile's first row and ends at the segment's end, so the hardware range check
+// returns zeros for rows past the segment: no branches, no per-row address arithmetic.
+// One sample's segment spans < 2^31 bytes (checked by the caller): 32-bit offsets.
 __device__ __forceinline__ void tile_rsrc(const Segments& S, int it, __amdgpu_buffer_rsrc_t& rk,
                                           __amdgpu_buffer_rsrc_t& rv) {
   const bool pre = it < S.ntiles[0];
   const int tl = pre ? it : it - S.ntiles[0];
   const int rows = (pre ? S.len[0] : S.len[1]) - tl * kBN;
-  // one sample's segment spans < 2^31 bytes (checked by the caller), so 32-bit offsets
   const uint32_t off = (uint32_t)tl * S.tile_bytes;
-  const uint32_t nbytes = (uint32_t)(rows < kBN ? rows : kBN) * S.row_bytes32;
+  const uint32_t nbytes = (uint32_t)(rows < kBN ? rows : kBN) * S.row_bytes;
   rk = make_rsrc((pre ? S.kbase[0] : S.kbase[1]) + off, nbytes);
   rv = make_rsrc((pre ? S.vbase[0] : S.vbase[1]) + off, nbytes);
 }
 
-__device__ __forceinline__ int tile_valid(const Segments& S, int it) {
-  const int seg = it < S.ntiles[0] ? 0 : 1;
-  const int tl = seg == 0 ? it : it - S.ntiles[0];
-  return S.len[seg] - tl * kBN;
+// valid keys of 32-key sub-tile s (may be <= 0 on a segment's last LDS tile)
+__device__ __forceinline__ int sub_valid(const Segments& S, int s) {
+  const int it = s >> 1;
+  const bool pre = it < S.ntiles[0];
+  const int tl = pre ? it : it - S.ntiles[0];
+  return (pre ? S.len[0] : S.len[1]) - tl * kBN - (s & 1) * 32;
 }
-
-// Staging: thread t moves 16-byte chunks q = t and t + 512 of one K tile and one V tile
-// (row q / 16, chunk q % 16) from HBM to registers, then to their swizzled LDS slots.
-struct Stage {
-  uint4 k[2], v[2];
-};
-
-// LDS: two K tiles and two V tiles.  Iteration t computes tile t's scores (K buffer
-// t % 2) and tile t-1's PV product (V buffer (t-1) % 2) while tile t+1's K and tile t's
-// V are staged into the other buffers.
-constexpr int kLdsBytes = 4 * kTileBytes;  // 64 KB
 
 __global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_img,
@@ -130,7 +129,16 @@ __global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
     const int32_t* __restrict__ cu_p, int Hq, int Hkv, int n_cg, int max_q, int max_p,
     int64_t Tq, int64_t Tp, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
+  // six separate LDS objects, so the compiler sees that a tile load into one buffer
+  // cannot alias fragment reads from another and does not wait for it
+  __shared__ __attribute__((aligned(1024))) uint8_t lk0[kTileBytes], lk1[kTileBytes],
+      lk2[kTileBytes], lv0[kTileBytes], lv1[kTileBytes], lv2[kTileBytes];
+  auto kbuf = [&](int b) __attribute__((always_inline)) -> uint8_t* {
+    return b == 0 ? lk0 : (b == 1 ? lk1 : lk2);
+  };
+  auto vbuf = [&](int b) __attribute__((always_inline)) -> uint8_t* {
+    return b == 0 ? lv0 : (b == 1 ? lv1 : lv2);
+  };
 
   const uint32_t id = xcd_remap(blockIdx.x, gridDim.x);
   const int cg = (int)(id % (uint32_t)n_cg);
@@ -161,9 +169,8 @@ __global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
   const bool qvalid = active && qi < N;
 
   Segments S;
-  S.row_bytes = (int64_t)Hkv * kHeadDim * 2;
-  S.row_bytes32 = (uint32_t)S.row_bytes;
-  S.tile_bytes = (uint32_t)S.row_bytes * kBN;
+  S.row_bytes = (uint32_t)Hkv * kHeadDim * 2;
+  S.tile_bytes = S.row_bytes * kBN;
   S.kbase[0] = reinterpret_cast<const uint8_t*>(k_pre + (pa * Hkv + g) * kHeadDim);
   S.vbase[0] = reinterpret_cast<const uint8_t*>(v_pre + (pa * Hkv + g) * kHeadDim);
   S.kbase[1] = reinterpret_cast<const uint8_t*>(k_img + (qa * Hkv + g) * kHeadDim);
@@ -173,27 +180,30 @@ __global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
   S.ntiles[0] = (P + kBN - 1) / kBN;
   S.ntiles[1] = (N + kBN - 1) / kBN;
   const int ntiles = S.ntiles[0] + S.ntiles[1];
+  const int nsub = 2 * ntiles;  // 32-key sub-tiles (trailing ones may be fully masked)
 
-  // staging offsets: global (inside a tile) and LDS (inside a tile)
-  int goff[2], soff[2];
+  // staging: wave w fills 1 KB blocks 2w and 2w+1 of each tile (rows 4*blk .. +3); lane
+  // L of block blk lands in row 4*blk + L/16, slot L%16 and so fetches chunk
+  // (L%16) ^ swz(row) of that row
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  int goff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int qc = tid + kThreads * i;
-    const int row = qc >> 4, chunk = qc & 15;
-    goff[i] = row * (int)S.row_bytes + chunk * 16;
-    soff[i] = row * kRowBytes + ((chunk ^ swz(row)) << 4);
+    const int row = 4 * (2 * wave + i) + (lane >> 4);
+    goff[i] = row * (int)S.row_bytes + (((lane & 15) ^ swz(row)) << 4);
   }
 
-  // K-fragment reads (A operand of S^T = K Q^T): row kb*32 + col, chunk 2*st + hl.  The
-  // swizzle depends on row % 16 only, so kb adds the constant 32 rows (immediate offset).
-  const int j16 = lane & 15, grp = (lane >> 4) & 1;
+  // K-fragment reads (A operand of S^T = K Q^T): row 32*half + col, chunk 2*st + hl.  The
+  // swizzle depends on row % 16 only, so the half adds a constant 32 rows.
   int kofs[8];
 #pragma unroll
-  for (int st = 0; st < 8; ++st) kofs[st] = col * kRowBytes + (((2 * st + hl) ^ swz(col)) << 4);
+  for (int st = 0; st < 8; ++st) kofs[st] = col * kRow + (((2 * st + hl) ^ swz(col)) << 4);
   // V-fragment reads (A operand of O^T = V^T P^T, transposed): within each 16-lane group,
   // lane j addresses row key0 + j/4 at dims dim0 + 4*(j%4) and receives dim dim0 + j of
-  // rows key0 .. key0+3.  For step u, read r and dim block db: key0 = 32*(u/2) + 16*(u%2)
-  // + 8*r + 4*hl, dim0 = 32*db + 16*grp.  The u part is a multiple of 16 rows (immediate).
+  // rows key0 .. key0+3.  For sub-tile half h, step u, read r and dim block db:
+  // key0 = 32*h + 16*u + 8*r + 4*hl, dim0 = 32*db + 16*grp; h and u add multiples of 16
+  // rows (constant offsets).
+  const int j16 = lane & 15, grp = (lane >> 4) & 1;
   int vofs[2][4];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
@@ -201,7 +211,7 @@ __global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const int chunk = 4 * db + 2 * grp + ((j16 & 3) >> 1);
-      vofs[r][db] = row * kRowBytes + ((chunk ^ swz(row)) << 4) + ((j16 & 1) << 3);
+      vofs[r][db] = row * kRow + ((chunk ^ swz(row)) << 4) + ((j16 & 1) << 3);
     }
   }
 
@@ -224,112 +234,94 @@ __global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
   // m: reference maximum (log2 units); every weight exp2(s*c - m) is kept <= 2^8
   float m = -INFINITY, lsum = 0.0f;
 
-  Stage R;
-  auto load_k = [&](int t) {
+  // K (V) tile t into K (V) buffer buf, straight from HBM/L2 into LDS
+  auto load_k = [&](int t, int buf) {
     __amdgpu_buffer_rsrc_t rk, rv;
     tile_rsrc(S, t, rk, rv);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) R.k[i] = buf_load16(rk, goff[i]);
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (__attribute__((address_space(3))) void*)(kbuf(buf) + (2 * wave_u + i) * 1024),
+          16, goff[i], 0, 0, 0);
   };
-  auto load_v = [&](int t) {
+  auto load_v = [&](int t, int buf) {
     __amdgpu_buffer_rsrc_t rk, rv;
     tile_rsrc(S, t, rk, rv);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) R.v[i] = buf_load16(rv, goff[i]);
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (__attribute__((address_space(3))) void*)(vbuf(buf) + (2 * wave_u + i) * 1024),
+          16, goff[i], 0, 0, 0);
   };
-  auto store_k = [&](uint8_t* base) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(base + soff[i]) = R.k[i];
+  // fragment reads from K buffer kb / V buffer vb, sub-tile half h
+  auto kread = [&](int kb, int h, int st) -> bf16x8 {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(kbuf(kb) + h * 32 * kRow + kofs[st]));
   };
-  auto store_v = [&](uint8_t* base) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(base + soff[i]) = R.v[i];
-  };
-
-  // scores of one tile from the K tile at Ks (16 MFMAs, two interleaved chains)
-  auto qk = [&](const uint8_t* Ks, f32x16 (&sacc)[2]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
-#pragma unroll
-    for (int st = 0; st < 8; ++st)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = as_bf16x8(
-            *reinterpret_cast<const uint4*>(Ks + kofs[st] + kb * 32 * kRowBytes));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], sacc[kb], 0, 0, 0);
-      }
+  // V^T fragment for step u (16 keys) and dim block db: two transposed 8-byte reads
+  auto vread = [&](const uint8_t* vb, int u, int db) -> bf16x8 {
+    const uint8_t* p = vb + 16 * u * kRow;
+    const uint2 lo = __builtin_bit_cast(
+        uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + vofs[0][db])));
+    const uint2 hi = __builtin_bit_cast(
+        uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + vofs[1][db])));
+    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
   };
 
-  // keys past the end of the segment (its last tile only) score -inf
-  auto mask = [&](int t, f32x16 (&sacc)[2]) {
-    const int nvalid = tile_valid(S, t);
-    if (nvalid < kBN) {
+  // keys of sub-tile s past its segment's end score -inf
+  auto mask = [&](int s, f32x16& sacc) {
+    const int nvalid = sub_valid(S, s);
+    if (nvalid < 32) {
+      // key = (r/4)*8 + hl*4 + r%4; compare its constant part with one limit
+      const int lim = nvalid - hl * 4;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-          if (key >= nvalid) sacc[kb][r] = -INFINITY;
-        }
+      for (int r = 0; r < 16; ++r)
+        if ((r >> 2) * 8 + (r & 3) >= lim) sacc[r] = -INFINITY;
     }
   };
 
-  // P = exp2(s*c - m) in bf16 and the row sum of the same rounded weights (v_dot2 against
-  // (1, 1)), so the normalised weights sum to one exactly.  Returns this tile's sum.
-  auto exp_tile = [&](const f32x16 (&sacc)[2], bf16x8 (&pw)[4]) -> float {
-    float tsum = 0.0f;
+  // two weights p = exp2(s*c - m) as one packed bf16 word, and the row sum of the same
+  // rounded weights (v_dot2 against (1, 1)) so the normalised weights sum to one.
+  // Pair i of 8: PV step u = i/4, word i%4.
+  auto exp_pair = [&](const f32x16& sacc, int i, uint32_t (&pk)[2][4], float& tsum) {
+    const int u = i >> 2, e = (i & 3) * 2;
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[u * 8 + e], scale_log2, -m));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[u * 8 + e + 1], scale_log2, -m));
+    pk[u][i & 3] = pack_bf16x2(p0, p1);
+    tsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[u][i & 3]), kOnes2, tsum,
+                                           false);
+  };
+  auto pack_p = [&](const uint32_t (&pk)[2][4], bf16x8 (&pw)[2]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      uint32_t pk[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[u >> 1][(u & 1) * 8 + e], scale_log2, -m));
-        const float p1 =
-            __builtin_amdgcn_exp2f(fmaf(sacc[u >> 1][(u & 1) * 8 + e + 1], scale_log2, -m));
-        pk[e >> 1] = pack_bf16x2(p0, p1);
-        tsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e >> 1]), kOnes2,
-                                               tsum, false);
-      }
-      pw[u] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
-    }
-    return tsum;
+    for (int u = 0; u < 2; ++u) pw[u] = as_bf16x8(make_uint4(pk[u][0], pk[u][1], pk[u][2], pk[u][3]));
   };
 
-  // O^T += V^T P^T from the V tile at Vs (16 MFMAs, four chains).  k-slot (hl, e) of
-  // step u is key 32*(u/2) + 16*(u%2) + 4*hl + 8*(e/4) + e%4.
-  auto pv = [&](const uint8_t* Vs, const bf16x8 (&pw)[4]) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint8_t* vu = Vs + (32 * (u >> 1) + 16 * (u & 1)) * kRowBytes;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vu + vofs[0][db]));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vu + vofs[1][db]));
-        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-        const bf16x8 av = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pw[u], o[db], 0, 0, 0);
-      }
-    }
+  // Pipeline over 32-key sub-tiles.  Slot i (0..7) of the step at sub-tile s issues one
+  // MFMA of the scores of sub-tile s+1 (one chain), one MFMA of the PV product of
+  // sub-tile s-1 (four chains; k-slot (hl, e) of step u is key 16*u + 4*hl + 8*(e/4) +
+  // e%4) and one pair of weights of sub-tile s.  On the first step the "previous" P is
+  // all zeros (against V tile 0, already staged and finite); on the last step the scores
+  // of the non-existent next sub-tile come from a resident K buffer and are discarded.
+  // The LDS operands of each slot are read kPrefetch slots ahead into a ring of four;
+  // every such read targets a tile that is already resident (see the staging order).
+  // The common path uses the running reference m as is: if the sub-tile's sum of rounded
+  // weights stays <= 2^8 on every lane, no weight exceeds 2^8.  Otherwise (the first
+  // sub-tile, or a new larger score) the true maximum is taken, O and l are rescaled --
+  // after the PV product of s-1, which used the old m -- and the weights are recomputed.
+  bf16x8 kf[4], vf[4];
+  // LDS buffers are compile-time constants at every call site below, so each address is
+  // this lane's base plus an immediate offset
+  auto fetch = [&](int kb, int khalf, int vb, int vhalf, int i, int r)
+                   __attribute__((always_inline)) {
+    kf[r] = kread(kb, khalf, i);
+    vf[r] = vread(vbuf(vb) + vhalf * 32 * kRow, i >> 2, i & 3);
   };
-
-  // Softmax weights of the current tile, with the previous tile's PV product issued
-  // first so the exponentials run in its shadow.  The common path uses the running
-  // reference m as is: if this tile's sum of rounded weights stays <= 2^8 on every
-  // lane, no weight exceeds 2^8 and nothing else is needed.  Otherwise (the first tile,
-  // or a new larger score), the true maximum is taken, O and l are rescaled -- after
-  // the previous PV product, which used the old m -- and the weights are recomputed.
-  auto softmax_pv = [&](const f32x16 (&sacc)[2], bf16x8 (&pw)[4], const uint8_t* Vprev,
-                        const bf16x8 (&pprev)[4], bool have_prev) {
-    if (have_prev) pv(Vprev, pprev);
-    float tsum = exp_tile(sacc, pw);
+  auto finish_step = [&](int s, f32x16& scur, f32x16& snext, bf16x8 (&pcur)[2],
+                         uint32_t (&pk)[2][4], float tsum) {
+    pack_p(pk, pcur);
     if (__ballot(!(tsum <= kTwoTau)) != 0) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float mnew = fmaxf(m, mx * scale_log2);
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);
@@ -339,51 +331,99 @@ __global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       m = mnew;
-      tsum = exp_tile(sacc, pw);
+      tsum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) exp_pair(scur, i, pk, tsum);
+      pack_p(pk, pcur);
     }
     lsum += tsum;
+    mask(s + 1, snext);
   };
 
-  uint8_t* const kb0 = smem;
-  uint8_t* const kb1 = smem + kTileBytes;
-  uint8_t* const vb0 = smem + 2 * kTileBytes;
-  uint8_t* const vb1 = smem + 3 * kTileBytes;
 
-  // prologue: K(0) in LDS
-  load_k(0);
-  store_k(kb0);
+  // prologue: K tiles 0 and 1, V tile 0; V buffer 2 cleared (the first step's PV
+  // product reads it against an all-zero P); scores of sub-tile 0
+  load_k(0, 0);
+  load_v(0, 0);
+  if (ntiles > 1) load_k(1, 1);
+  for (int i = tid; i < kTileBytes / 16; i += kThreads)
+    reinterpret_cast<uint4*>(lv2)[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
+  const f32x16 zero16 = {};
+  f32x16 sa, sb;
+  bf16x8 pa_[2], pb2[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) pb2[u] = as_bf16x8(make_uint4(0, 0, 0, 0));
+  if (active) {
+    sa = zero16;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(0, 0, i), qf[i], sa, 0, 0, 0);
+    mask(0, sa);
+    // operands of the first slots of iteration 0: K tile 0 (second half), V "tile -1"
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) fetch(0, 1, 2, 1, k, k & 3);
+  }
 
-  f32x16 sacc[2];
-  bf16x8 pa_[4], pb2[4];  // P of even / odd tiles
-
-  // iteration t: stage K(t+1), V(t); scores of tile t; PV of tile t-1 with tile t's
-  // softmax.  Kcur/Knext and Vprev/Vcur alternate with the parity of t.
-  auto iteration = [&](int t, const uint8_t* Kcur, uint8_t* Knext, const uint8_t* Vprev,
-                       uint8_t* Vcur, bf16x8 (&pcur)[4], const bf16x8 (&pprev)[4]) {
-    const bool kmore = t + 1 < ntiles;
-    if (kmore) load_k(t + 1);
-    load_v(t);
+  // iteration T: steps at sub-tiles 2T (scores in sa) and 2T+1; stage K tile T+2 and V
+  // tile T+1.  Tile t lives in buffer t % 3 (T3 = T % 3 is a compile-time constant).
+  // Reads in iteration T touch K tiles T, T+1 and V tiles T-1, T; the reads prefetched
+  // for the first slots of iteration T+1 touch K tile T+1 and V tile T; the stores go to
+  // the buffers of K tile T-1 and V tile T-2, which nothing reads any more.
+  auto iteration = [&](int T, auto t3) __attribute__((always_inline)) {
+    constexpr int T3 = decltype(t3)::value;
+    constexpr int b0 = T3, b1 = (T3 + 1) % 3, bm1 = (T3 + 2) % 3;
+    const bool kmore = T + 2 < ntiles, vmore = T + 1 < ntiles;
+    if (kmore) load_k(T + 2, bm1);
+    if (vmore) load_v(T + 1, b1);
     if (active) {
-      qk(Kcur, sacc);
-      mask(t, sacc);
-      softmax_pv(sacc, pcur, Vprev, pprev, t > 0);
+      uint32_t pk[2][4];
+      float tsum = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int h = k >> 3, i = k & 7;
+        f32x16& scur = h == 0 ? sa : sb;
+        f32x16& snext = h == 0 ? sb : sa;
+        bf16x8 (&pcur)[2] = h == 0 ? pa_ : pb2;
+        bf16x8 (&pprev)[2] = h == 0 ? pb2 : pa_;
+        if (i == 0) tsum = 0.0f;
+        {
+          const int kk = k + kPrefetch;
+          if (kk < 8)  // step at sub-tile 2T: K of 2T+1, V of 2T-1
+            fetch(b0, 1, bm1, 1, kk, kk & 3);
+          else if (kk < 16)  // step at sub-tile 2T+1: K of 2T+2, V of 2T
+            fetch(b1, 0, b0, 0, kk - 8, kk & 3);
+          else  // first step of iteration T+1: K of 2T+3, V of 2T+1
+            fetch(b1, 1, b0, 1, kk - 16, kk & 3);
+        }
+        snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k & 3], qf[i], i == 0 ? zero16 : snext,
+                                                        0, 0, 0);
+        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[k & 3], pprev[i >> 2], o[i & 3], 0, 0, 0);
+        exp_pair(scur, i, pk, tsum);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i == 7) finish_step(2 * T + h, scur, snext, pcur, pk, tsum);
+      }
     }
-    if (kmore) store_k(Knext);
-    store_v(Vcur);
     __syncthreads();
   };
-
-  int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
-    iteration(t, kb0, kb1, vb1, vb0, pa_, pb2);
-    iteration(t + 1, kb1, kb0, vb0, vb1, pb2, pa_);
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  for (int T = 0; T < ntiles; T += 3) {
+    iteration(T, C0{});
+    if (T + 1 >= ntiles) break;
+    iteration(T + 1, C1{});
+    if (T + 2 >= ntiles) break;
+    iteration(T + 2, C2{});
   }
-  if (t < ntiles) {
-    iteration(t, kb0, kb1, vb1, vb0, pa_, pb2);
-    if (active) pv(vb0, pa_);
-  } else if (active) {
-    pv(vb1, pb2);
+  // last sub-tile's PV product (its P is in pb2)
+  if (active) {
+    // sub-tile nsub-1 is the second half of tile ntiles-1
+    const uint8_t* va = vbuf((ntiles - 1) % 3) + 32 * kRow;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(va, i >> 2, i & 3), pb2[i >> 2],
+                                                         o[i & 3], 0, 0, 0);
   }
 
   const float ltot = lsum + __shfl_xor(lsum, 32);
