@@ -59,6 +59,9 @@ def _load():
                                         ctypes.c_double, _lp, ctypes.c_int64, _dp, _dp]
         lib.oracle_euler_step.argtypes = [_dp, _dp, ctypes.c_int64, ctypes.c_double,
                                           ctypes.c_double, ctypes.c_double]
+        lib.oracle_cfg_path.restype = ctypes.c_int
+        lib.oracle_cfg_path.argtypes = [ctypes.c_double] * 5
+        lib.oracle_euler_step_cfg.argtypes = [_dp, _dp, _dp, _dp, ctypes.c_int64] + [ctypes.c_double] * 7
         _lib = lib
     return _lib
 
@@ -163,4 +166,32 @@ def euler_step(z, x0, t, t_next, t_eps=0.02) -> np.ndarray:
     assert z.shape == x0.shape
     _load().oracle_euler_step(_ptr(z, _dp), _ptr(x0, _dp), z.size, float(t), float(t_next),
                               float(t_eps))
+    return z
+
+
+def cfg_path(t, cfg_scale, img_cfg_scale, cfg_interval=(0.0, 1.0)) -> int:
+    """Guidance path 1..4 of a step; [B] §2.7 (the four code paths)."""
+    return int(_load().oracle_cfg_path(float(t), float(cfg_scale), float(img_cfg_scale),
+                                       float(cfg_interval[0]), float(cfg_interval[1])))
+
+
+def euler_step_cfg(z, x0_cond, x0_text_uncond=None, x0_uncond=None, *, t, t_next, t_eps=0.02,
+                   cfg_scale=4.0, img_cfg_scale=1.0, cfg_interval=(0.0, 1.0)) -> np.ndarray:
+    """Three-branch classifier-free guidance, then one Euler step; [B] §2.7.
+
+    Branch predictions the selected path does not read may be None."""
+    z = _f64(z).copy()
+    xc = _f64(x0_cond)
+    path = cfg_path(t, cfg_scale, img_cfg_scale, cfg_interval)
+    need_tu, need_u = path in (2, 4), path in (3, 4)
+    if (need_tu and x0_text_uncond is None) or (need_u and x0_uncond is None):
+        raise ValueError(f"guidance path {path} needs the missing branch prediction")
+    xtu = _f64(x0_text_uncond) if x0_text_uncond is not None else None
+    xu = _f64(x0_uncond) if x0_uncond is not None else None
+    for x in (xc, xtu, xu):
+        assert x is None or x.shape == z.shape
+    _load().oracle_euler_step_cfg(
+        _ptr(z, _dp), _ptr(xc, _dp), _ptr(xtu, _dp) if xtu is not None else None,
+        _ptr(xu, _dp) if xu is not None else None, z.size, float(t), float(t_next), float(t_eps),
+        float(cfg_scale), float(img_cfg_scale), float(cfg_interval[0]), float(cfg_interval[1]))
     return z

@@ -206,3 +206,68 @@ void oracle_euler_step(double *z, const double *x0, int64_t n,
         z[i] = z[i] + (t_next - t) * v;
     }
 }
+
+/*
+ * Which guidance path a step takes, [B] §2.7 (the four code paths of the
+ * three-branch guidance in the main loop).  Guidance is on when t lies strictly
+ * inside the interval (lo, hi), or always when the interval starts at 0.
+ *   1: guidance off, or gamma == gamma_img == 1   (one forward: cond)
+ *   2: gamma_img == 1                             (cond and text-uncond)
+ *   3: gamma == gamma_img                         (cond and full uncond)
+ *   4: otherwise                                  (all three branches)
+ * The comparisons are exact, as on the pages.
+ */
+int oracle_cfg_path(double t, double gamma, double gamma_img, double lo, double hi)
+{
+    int use_cfg = (t > lo && t < hi) || lo == 0.0;
+    if (!use_cfg || (gamma == 1.0 && gamma_img == 1.0))
+        return 1;
+    if (gamma_img == 1.0)
+        return 2;
+    if (gamma == gamma_img)
+        return 3;
+    return 4;
+}
+
+/*
+ * Classifier-free guidance over the conditioning branches, then one Euler step:
+ * [B] §2.7 (three KV caches -- cond, text-uncond with the image context kept,
+ * full uncond -- one forward each per step, combined by the three-branch
+ * guidance formula) and [A] §Flow matching without a VAE (each branch's head
+ * predicts x0, which the sampler turns into a velocity for the shared z).
+ * Per element, in the pages' order: every needed branch's velocity
+ * v_b = (x0_b - z) / max(1 - t, t_eps), then
+ *   path 1: v = v_c
+ *   path 2: v = v_tu + gamma (v_c - v_tu)
+ *   path 3: v = v_u  + gamma (v_c - v_u)
+ *   path 4: v = v_u  + gamma (v_c - v_tu) + gamma_img (v_tu - v_u)
+ * and z <- z + (t_next - t) v.  Branch inputs the path does not read may be
+ * NULL.
+ */
+void oracle_euler_step_cfg(double *z, const double *x0_c, const double *x0_tu,
+                           const double *x0_u, int64_t n, double t, double t_next,
+                           double t_eps, double gamma, double gamma_img, double lo,
+                           double hi)
+{
+    double denom = fmax(1.0 - t, t_eps);
+    int path = oracle_cfg_path(t, gamma, gamma_img, lo, hi);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        double v_c = (x0_c[i] - z[i]) / denom;
+        double v;
+        if (path == 1) {
+            v = v_c;
+        } else if (path == 2) {
+            double v_tu = (x0_tu[i] - z[i]) / denom;
+            v = v_tu + gamma * (v_c - v_tu);
+        } else if (path == 3) {
+            double v_u = (x0_u[i] - z[i]) / denom;
+            v = v_u + gamma * (v_c - v_u);
+        } else {
+            double v_tu = (x0_tu[i] - z[i]) / denom;
+            double v_u = (x0_u[i] - z[i]) / denom;
+            v = v_u + gamma * (v_c - v_tu) + gamma_img * (v_tu - v_u);
+        }
+        z[i] = z[i] + (t_next - t) * v;
+    }
+}

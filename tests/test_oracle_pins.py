@@ -364,3 +364,77 @@ def test_attn_sampled_rows_match_full():
     part, lse_p = oracle.gen_attn(**a, tokens=rows, with_lse=True)
     np.testing.assert_array_equal(part, full[rows])
     np.testing.assert_array_equal(lse_p, lse[rows])
+
+
+# --------------------------------------------------------------------------------------
+# Classifier-free guidance + Euler step: [B] §2.7 (three branches, four code paths)
+# --------------------------------------------------------------------------------------
+
+def test_cfg_worked_examples():
+    """Hand-worked step on every guidance path and both interval rules (golden fixture);
+    catches a wrong sign, a swapped branch or a wrong interval rule."""
+    g = _golden("cfg_worked.json")
+    for c in g["cases"]:
+        iv = tuple(c["cfg_interval"])
+        assert oracle.cfg_path(g["t"], c["cfg_scale"], c["img_cfg_scale"], iv) == c["path"], c
+        z1 = oracle.euler_step_cfg([g["z"]], [g["x0_cond"]], [g["x0_text_uncond"]],
+                                   [g["x0_uncond"]], t=g["t"], t_next=g["t_next"],
+                                   t_eps=g["t_eps"], cfg_scale=c["cfg_scale"],
+                                   img_cfg_scale=c["img_cfg_scale"], cfg_interval=iv)[0]
+        assert z1 == c["z_next"], (c, z1)
+
+
+def test_cfg_weights_sum_to_one():
+    """Invariant: every path is an affine combination of the branch velocities, so when
+    all branches predict the same x0 the step is the single-branch Euler step."""
+    rng = np.random.default_rng(7)
+    z, x = rng.standard_normal(257), rng.standard_normal(257)
+    for gam, gim, iv in [(4.0, 1.0, (0, 1)), (3.0, 3.0, (0, 1)), (4.0, 1.5, (0, 1)),
+                         (7.5, -2.0, (0, 1)), (4.0, 1.5, (0.7, 1.0))]:
+        for t, tn in [(0.1, 0.15), (0.6, 0.7), (0.99, 1.0)]:
+            got = oracle.euler_step_cfg(z, x, x, x, t=t, t_next=tn, cfg_scale=gam,
+                                        img_cfg_scale=gim, cfg_interval=iv)
+            ref = oracle.euler_step(z, x, t, tn)
+            np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_cfg_paths_are_continuous():
+    """Paths 1-3 are the reductions of the full three-branch formula named on the pages
+    (gamma_img = 1; gamma = gamma_img; both 1); the fast paths must agree with the full
+    formula just off those lines -- catches a fast path with a wrong branch or term."""
+    rng = np.random.default_rng(11)
+    z, xc, xtu, xu = (rng.standard_normal(129) for _ in range(4))
+    kw = dict(t=0.3, t_next=0.35)
+    eps = 1e-9
+    pairs = [((4.0, 1.0), (4.0, 1.0 + eps)), ((3.0, 3.0), (3.0, 3.0 + eps)),
+             ((1.0, 1.0), (1.0 + eps, 1.0 + 2 * eps))]
+    for (g1, i1), (g2, i2) in pairs:
+        fast = oracle.euler_step_cfg(z, xc, xtu, xu, cfg_scale=g1, img_cfg_scale=i1, **kw)
+        full = oracle.euler_step_cfg(z, xc, xtu, xu, cfg_scale=g2, img_cfg_scale=i2, **kw)
+        assert oracle.cfg_path(kw["t"], g2, i2) == 4 and oracle.cfg_path(kw["t"], g1, i1) != 4
+        np.testing.assert_allclose(fast, full, rtol=0, atol=1e-6)
+
+
+def test_cfg_in_x0_space():
+    """Property: the guidance weights of each path sum to one, so guiding the x0
+    predictions with the same weights and then taking one plain Euler step gives the
+    same z (the combine can be fused into the Euler pass)."""
+    rng = np.random.default_rng(3)
+    z, xc, xtu, xu = (rng.standard_normal(300) for _ in range(4))
+    t, tn = 0.42, 0.47
+    for gam, gim, w in [(4.0, 1.0, (4.0, -3.0, 0.0)), (2.5, 2.5, (2.5, 0.0, -1.5)),
+                        (4.0, 1.5, (4.0, -2.5, -0.5))]:
+        assert abs(sum(w) - 1.0) < 1e-15
+        xg = w[0] * xc + w[1] * xtu + w[2] * xu
+        got = oracle.euler_step_cfg(z, xc, xtu, xu, t=t, t_next=tn, cfg_scale=gam,
+                                    img_cfg_scale=gim)
+        np.testing.assert_allclose(got, oracle.euler_step(z, xg, t, tn), rtol=0, atol=1e-12)
+
+
+def test_cfg_missing_branch_is_an_error():
+    with pytest.raises(ValueError):
+        oracle.euler_step_cfg([0.0], [1.0], None, None, t=0.5, t_next=0.6, cfg_scale=4.0,
+                              img_cfg_scale=1.0)
+    # path 1 reads the conditional branch only
+    assert oracle.euler_step_cfg([0.0], [1.0], None, None, t=0.5, t_next=0.75, cfg_scale=1.0,
+                                 img_cfg_scale=1.0)[0] == 0.5
