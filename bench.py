@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--workload", default="large", choices=["large", "mid", "small", "editing"])
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cfg-steps", type=int, default=100,
+                    help="timed calls of the guided Euler step per guidance path (0 skips it)")
     ap.add_argument("--cpu-tokens", type=int, default=256,
                     help="query tokens in the oracle's attention sample")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -255,6 +257,41 @@ def main():
     gpu_step_s = float((pro_ms + att_ms + eul_ms).mean()) * 1e-3
     roof_step_s = flops / (PEAK_BF16_TFLOPS * 1e12) + (pro_bytes + euler_bytes) / (PEAK_HBM_GBS * 1e9)
 
+    # the guided step of the next row: guidance over the branches' x0 fused with the
+    # Euler update, on the pages' text-to-image path (2 branches) and the full 3-branch path
+    cfg = {}
+    if a.cfg_steps > 0:
+        x_tu, x_u = W.cfg_branches(w)
+        xtu_d, xu_d = H.dev_f32(x_tu), H.dev_f32(x_u)
+        for k_, s_ in enumerate(sets):
+            s_["xtu"] = xtu_d.roll(k_).contiguous()
+            s_["xu"] = xu_d.roll(k_).contiguous()
+        del xtu_d, xu_d
+        npx = int(np.prod(w.pixel_shape))
+        for label, g, gi, nbr in (("path2_text_to_image", 4.0, 1.0, 2), ("path4_three_branch", 4.0, 1.5, 3)):
+            assert neo.cfg_path(t, g, gi) == (2 if nbr == 2 else 4)
+
+            def cfg_step(i):
+                s_ = sets[i % len(sets)]
+                neo.fm_euler_step_cfg(s_["z"], s_["x"], s_["xtu"], s_["xu"], t=t, t_next=tn,
+                                      t_eps=w.t_eps, cfg_scale=g, img_cfg_scale=gi)
+            for i in range(10):
+                cfg_step(i)
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(a.cfg_steps)]
+            torch.cuda.synchronize()
+            for i in range(a.cfg_steps):
+                evs[i][0].record()
+                cfg_step(i)
+                evs[i][1].record()
+            torch.cuda.synchronize()
+            us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
+            nbytes = npx * 4 * (nbr + 2)
+            cfg[label] = {"us": us, "bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
+                          "hbm_frac": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+        print(f"[bench] guided Euler step timed ({a.cfg_steps} calls per path)", file=sys.stderr,
+              flush=True)
+
     cpu = None
     if not a.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
@@ -292,6 +329,7 @@ def main():
         "hbm_frac": {"qknorm_rope3": pro_gbs / PEAK_HBM_GBS, "fm_euler_step": eul_gbs / PEAK_HBM_GBS},
         "step_roofline": {"tokens_per_s_at_roofline": ntok / roof_step_s,
                           "frac": (ntok / gpu_step_s) / (ntok / roof_step_s)},
+        "cfg_euler": cfg,
     }
     print(json.dumps(result), flush=True)
 

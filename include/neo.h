@@ -158,6 +158,51 @@ neo_status neo_gen_attn_fwd(const void *q, const void *k_img, const void *v_img,
 neo_status neo_fm_euler_step(float *z, const float *x0_pred, int64_t n, float t, float t_next,
                              float t_eps, void *hip_stream);
 
+/*
+ * neo_cfg_path -- which classifier-free guidance path a flow step takes
+ * ([B] §2.7, the four code paths of the main loop).  Guidance is on when
+ * cfg_interval_lo < t < cfg_interval_hi, or always when cfg_interval_lo == 0;
+ * then, with exact comparisons as on the pages:
+ *   1  guidance off, or cfg_scale == img_cfg_scale == 1: one forward (cond)
+ *   2  img_cfg_scale == 1: cond and text-uncond (image context kept)
+ *   3  cfg_scale == img_cfg_scale: cond and full uncond
+ *   4  otherwise: all three branches
+ * A caller uses it to decide which branch forwards to run.  Pure host function.
+ */
+int neo_cfg_path(float t, float cfg_scale, float img_cfg_scale, float cfg_interval_lo,
+                 float cfg_interval_hi);
+
+/*
+ * neo_fm_euler_step_cfg -- classifier-free guidance over the branches' x0
+ * predictions fused with the x0-to-velocity Euler step, in place, one pass
+ * over the pixels ([B] §2.7: three-branch guidance; [A] §Flow matching without
+ * a VAE and §Runtime / metadata status: each branch predicts x0 for the same z
+ * from its own frozen prefix).  With v_b = (x0_b - z) / max(1 - t, t_eps):
+ *   path 1: v = v_c
+ *   path 2: v = v_tu + cfg_scale (v_c - v_tu)
+ *   path 3: v = v_u  + cfg_scale (v_c - v_u)
+ *   path 4: v = v_u  + cfg_scale (v_c - v_tu) + img_cfg_scale (v_tu - v_u)
+ * and z <- z + (t_next - t) v, the path chosen as neo_cfg_path does.  The
+ * weights of every path sum to one, so the library forms the guided x0 with
+ * those weights and takes one Euler step: z + c*(sum_b w_b x0_b - z), c and the
+ * weights computed once in double on the host, the pass in fp32.
+ *
+ *   z               [n] fp32, device: read and written.
+ *   x0_cond         [n] fp32, device: the conditional branch; always read.
+ *   x0_text_uncond  [n] fp32, device: read on paths 2 and 4, else may be NULL.
+ *   x0_uncond       [n] fp32, device: read on paths 3 and 4, else may be NULL.
+ *   The x0 inputs may alias one another or be exactly z; none may partially
+ *   overlap z.  All 4-byte aligned (16-byte alignment takes the vector path).
+ *   n >= 0 (0 is a no-op).  t, t_next finite, t <= t_next; t_eps > 0;
+ *   cfg_scale, img_cfg_scale and the interval bounds finite.
+ * Errors: NEO_ERR_SHAPE (n), NEO_ERR_VALUE (scalars, overlap, alignment),
+ * NEO_ERR_NULL (a branch the path reads is NULL), NEO_ERR_HIP (launch).
+ */
+neo_status neo_fm_euler_step_cfg(float *z, const float *x0_cond, const float *x0_text_uncond,
+                                 const float *x0_uncond, int64_t n, float t, float t_next,
+                                 float t_eps, float cfg_scale, float img_cfg_scale,
+                                 float cfg_interval_lo, float cfg_interval_hi, void *hip_stream);
+
 /* Static English text for a status code; never NULL. */
 const char *neo_status_string(neo_status s);
 

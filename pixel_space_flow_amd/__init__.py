@@ -13,8 +13,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["qknorm_rope3", "gen_attn_fwd", "fm_euler_step", "NeoError", "lib", "LIB_PATH",
-           "EXPORTED_SYMBOLS", "NEO_OK", "NEO_ERR_NULL", "NEO_ERR_SHAPE", "NEO_ERR_VALUE",
+__all__ = ["qknorm_rope3", "gen_attn_fwd", "fm_euler_step", "fm_euler_step_cfg", "cfg_path",
+           "NeoError", "lib", "LIB_PATH", "EXPORTED_SYMBOLS", "NEO_OK", "NEO_ERR_NULL", "NEO_ERR_SHAPE", "NEO_ERR_VALUE",
            "NEO_ERR_UNSUPPORTED", "NEO_ERR_HIP", "NEO_F32", "NEO_BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libneo.so")
@@ -23,7 +23,8 @@ NEO_OK, NEO_ERR_NULL, NEO_ERR_SHAPE, NEO_ERR_VALUE, NEO_ERR_UNSUPPORTED, NEO_ERR
 NEO_F32, NEO_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = ("neo_qknorm_rope3", "neo_gen_attn_fwd", "neo_fm_euler_step",
-                    "neo_status_string", "neo_last_error")
+                    "neo_cfg_path", "neo_fm_euler_step_cfg", "neo_status_string",
+                    "neo_last_error")
 
 _vp = ctypes.c_void_p
 _i32, _i64, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
@@ -54,6 +55,10 @@ def lib() -> ctypes.CDLL:
                                        _i64, _i64, _i32, _i32, _f32, _vp, _vp, ctypes.c_int, _vp]
         L.neo_fm_euler_step.restype = ctypes.c_int
         L.neo_fm_euler_step.argtypes = [_vp, _vp, _i64, _f32, _f32, _f32, _vp]
+        L.neo_cfg_path.restype = ctypes.c_int
+        L.neo_cfg_path.argtypes = [_f32] * 5
+        L.neo_fm_euler_step_cfg.restype = ctypes.c_int
+        L.neo_fm_euler_step_cfg.argtypes = [_vp, _vp, _vp, _vp, _i64] + [_f32] * 7 + [_vp]
         L.neo_status_string.restype = ctypes.c_char_p
         L.neo_status_string.argtypes = [ctypes.c_int]
         L.neo_last_error.restype = ctypes.c_char_p
@@ -178,4 +183,32 @@ def fm_euler_step(z, x0_pred, t, t_next, t_eps=0.02):
     st = lib().neo_fm_euler_step(z.data_ptr(), x0_pred.data_ptr(), z.numel(), float(t),
                                  float(t_next), float(t_eps), _stream(z))
     _check("neo_fm_euler_step", st)
+    return z
+
+
+def cfg_path(t, cfg_scale=4.0, img_cfg_scale=1.0, cfg_interval=(0.0, 1.0)) -> int:
+    """Guidance path 1..4 of a flow step ([B] §2.7): 1 = cond only, 2 = cond and
+    text-uncond, 3 = cond and full uncond, 4 = all three branches."""
+    return int(lib().neo_cfg_path(float(t), float(cfg_scale), float(img_cfg_scale),
+                                  float(cfg_interval[0]), float(cfg_interval[1])))
+
+
+def fm_euler_step_cfg(z, x0_cond, x0_text_uncond=None, x0_uncond=None, *, t, t_next,
+                      t_eps=0.02, cfg_scale=4.0, img_cfg_scale=1.0, cfg_interval=(0.0, 1.0)):
+    """In place: three-branch classifier-free guidance over the branches' x0
+    predictions fused with the Euler step ([B] §2.7).  Branches the guidance path
+    does not read (see cfg_path) may be None.  All tensors fp32 on the HIP device."""
+    torch = _torch()
+    _dev(z, "z", torch.float32)
+    xs = []
+    for name, x in (("x0_cond", x0_cond), ("x0_text_uncond", x0_text_uncond),
+                    ("x0_uncond", x0_uncond)):
+        if x is not None:
+            _dev(x, name, torch.float32, z.shape)
+        xs.append(x.data_ptr() if x is not None else None)
+    st = lib().neo_fm_euler_step_cfg(z.data_ptr(), xs[0], xs[1], xs[2], z.numel(), float(t),
+                                     float(t_next), float(t_eps), float(cfg_scale),
+                                     float(img_cfg_scale), float(cfg_interval[0]),
+                                     float(cfg_interval[1]), _stream(z))
+    _check("neo_fm_euler_step_cfg", st)
     return z

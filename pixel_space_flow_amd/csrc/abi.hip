@@ -202,4 +202,61 @@ neo_status neo_fm_euler_step(float* z, const float* x0_pred, int64_t n, float t,
                   "neo_fm_euler_step launch");
 }
 
+int neo_cfg_path(float t, float cfg_scale, float img_cfg_scale, float cfg_interval_lo,
+                 float cfg_interval_hi) {
+  // the pages' loop: guidance on strictly inside the interval, or always when the
+  // interval starts at 0; then the four cases by exact comparison of the scales
+  const bool use_cfg = (t > cfg_interval_lo && t < cfg_interval_hi) || cfg_interval_lo == 0.0f;
+  if (!use_cfg || (cfg_scale == 1.0f && img_cfg_scale == 1.0f)) return 1;
+  if (img_cfg_scale == 1.0f) return 2;
+  if (cfg_scale == img_cfg_scale) return 3;
+  return 4;
+}
+
+neo_status neo_fm_euler_step_cfg(float* z, const float* x0_cond, const float* x0_text_uncond,
+                                 const float* x0_uncond, int64_t n, float t, float t_next,
+                                 float t_eps, float cfg_scale, float img_cfg_scale,
+                                 float cfg_interval_lo, float cfg_interval_hi,
+                                 void* hip_stream) {
+  const char* fn = "neo_fm_euler_step_cfg";
+  if (n < 0 || n > INT64_MAX / 16) return fail(NEO_ERR_SHAPE, "%s: n=%lld out of range", fn, (long long)n);
+  if (!finite(t) || !finite(t_next) || !finite(t_eps))
+    return fail(NEO_ERR_VALUE, "%s: t, t_next, t_eps must be finite", fn);
+  if (!finite(cfg_scale) || !finite(img_cfg_scale) || !finite(cfg_interval_lo) ||
+      !finite(cfg_interval_hi))
+    return fail(NEO_ERR_VALUE, "%s: guidance scales and interval must be finite", fn);
+  if (t_eps <= 0.0f) return fail(NEO_ERR_VALUE, "%s: t_eps must be > 0", fn);
+  if (t_next < t) return fail(NEO_ERR_VALUE, "%s: t_next < t", fn);
+  const int path = neo_cfg_path(t, cfg_scale, img_cfg_scale, cfg_interval_lo, cfg_interval_hi);
+  if (n == 0) return ok();
+  // branch inputs and weights (they sum to one on every path)
+  const double g = cfg_scale, gi = img_cfg_scale;
+  const float* x[3] = {x0_cond, nullptr, nullptr};
+  double w[3] = {1.0, 0.0, 0.0};
+  int nb = 1;
+  if (path == 2) {
+    x[1] = x0_text_uncond; w[0] = g; w[1] = 1.0 - g; nb = 2;
+  } else if (path == 3) {
+    x[1] = x0_uncond; w[0] = g; w[1] = 1.0 - g; nb = 2;
+  } else if (path == 4) {
+    x[1] = x0_text_uncond; x[2] = x0_uncond; w[0] = g; w[1] = gi - g; w[2] = 1.0 - gi; nb = 3;
+  }
+  if (!z) return fail(NEO_ERR_NULL, "%s: z is NULL", fn);
+  for (int b = 0; b < nb; ++b)
+    if (!x[b]) return fail(NEO_ERR_NULL, "%s: guidance path %d reads a NULL branch", fn, path);
+  const size_t bytes = (size_t)n * sizeof(float);
+  uintptr_t bits = reinterpret_cast<uintptr_t>(z);
+  for (int b = 0; b < nb; ++b) {
+    if (static_cast<const void*>(x[b]) != static_cast<const void*>(z) && overlap(z, bytes, x[b], bytes))
+      return fail(NEO_ERR_VALUE, "%s: z and a branch input partially overlap", fn);
+    bits |= reinterpret_cast<uintptr_t>(x[b]);
+  }
+  if (bits & 3) return fail(NEO_ERR_VALUE, "%s: buffers must be 4-byte aligned", fn);
+  const double denom = fmax(1.0 - (double)t, (double)t_eps);
+  const float coef = (float)(((double)t_next - (double)t) / denom);
+  const float wf[3] = {(float)w[0], (float)w[1], (float)w[2]};
+  return from_hip(neo::launch_euler_step_cfg(z, x, wf, nb, n, coef, static_cast<hipStream_t>(hip_stream)),
+                  "neo_fm_euler_step_cfg launch");
+}
+
 }  // extern "C"

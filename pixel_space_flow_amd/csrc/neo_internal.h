@@ -33,6 +33,10 @@ hipError_t launch_gen_attn_f32(const float* q, const float* k_img, const float* 
 hipError_t launch_euler_step(float* z, const float* x0, int64_t n, float coef,
                              hipStream_t stream);
 
+// z <- z + coef * (sum_b w[b] * x[b] - z) over nb = 1..3 branch inputs
+hipError_t launch_euler_step_cfg(float* z, const float* const x[3], const float w[3], int nb,
+                                 int64_t n, float coef, hipStream_t stream);
+
 // ---- device helpers -----------------------------------------------------------------
 
 // bf16 <-> fp32 on raw 16-bit patterns.  The conversion to bf16 rounds to nearest

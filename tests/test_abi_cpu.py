@@ -5,6 +5,7 @@ import math
 import os
 import re
 
+import numpy as np
 import pytest
 
 import pixel_space_flow_amd as P
@@ -151,3 +152,54 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(P, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         P.lib()
+
+
+def _cfg(L, **kw):
+    a = dict(z=FAKE, xc=FAKE + (1 << 30), xtu=FAKE + (2 << 30), xu=FAKE + (3 << 30), n=1000,
+             t=0.5, tn=0.55, eps=0.02, g=4.0, gi=1.5, lo=0.0, hi=1.0)
+    a.update(kw)
+    return L.neo_fm_euler_step_cfg(a["z"], a["xc"], a["xtu"], a["xu"], a["n"], a["t"], a["tn"],
+                                   a["eps"], a["g"], a["gi"], a["lo"], a["hi"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), P.NEO_ERR_SHAPE),
+    (dict(tn=0.4), P.NEO_ERR_VALUE),                             # t_next < t
+    (dict(eps=0.0), P.NEO_ERR_VALUE),
+    (dict(g=math.nan), P.NEO_ERR_VALUE),
+    (dict(hi=math.inf), P.NEO_ERR_VALUE),
+    (dict(z=None), P.NEO_ERR_NULL),
+    (dict(xc=None), P.NEO_ERR_NULL),
+    (dict(xtu=None), P.NEO_ERR_NULL),                           # path 4 reads text-uncond
+    (dict(xu=None), P.NEO_ERR_NULL),                            # path 4 reads uncond
+    (dict(gi=1.0, xu=None, xtu=None), P.NEO_ERR_NULL),          # path 2 reads text-uncond
+    (dict(g=2.0, gi=2.0, xu=None), P.NEO_ERR_NULL),             # path 3 reads uncond
+    (dict(xtu=FAKE + 64), P.NEO_ERR_VALUE),                     # partial overlap with z
+    (dict(xc=FAKE + (1 << 30) + 2), P.NEO_ERR_VALUE),           # misaligned
+])
+def test_cfg_validation(L, kw, status):
+    assert _cfg(L, **kw) == status
+    assert L.neo_last_error().decode().startswith("neo_fm_euler_step_cfg")
+
+
+def test_cfg_unread_branches_may_be_null(L):
+    # each path leaves the branches it does not read unchecked; n = 0 launches nothing
+    assert _cfg(L, n=0, g=1.0, gi=1.0, xtu=None, xu=None) == P.NEO_OK
+    assert _cfg(L, n=0, gi=1.0, xu=None) == P.NEO_OK
+    assert _cfg(L, n=0, g=2.0, gi=2.0, xtu=None) == P.NEO_OK
+
+
+def test_cfg_path_matches_the_oracle_rule():
+    """The library's host-side path choice against the oracle's, on the pages' cases,
+    the interval rules and a sweep of scales."""
+    import oracle
+    cases = [(0.5, 1, 1, 0, 1), (0.5, 4, 1, 0, 1), (0.5, 3, 3, 0, 1), (0.5, 4, 1.5, 0, 1),
+             (0.5, 4, 1, 0.7, 1), (0.5, 4, 1, 0, 0.3), (0.5, 4, 1, 0.5, 1), (0.5, 4, 1, 0.2, 0.5),
+             (0.9, 4, 2, 0.1, 0.95), (0.05, 7, 7, 0.1, 0.95)]
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        cases.append((float(rng.uniform()), float(rng.choice([1.0, 2.0, 4.0])),
+                      float(rng.choice([1.0, 2.0, 1.5])), float(rng.choice([0.0, 0.25])),
+                      float(rng.choice([1.0, 0.75]))))
+    for t, g, gi, lo, hi in cases:
+        assert P.cfg_path(t, g, gi, (lo, hi)) == oracle.cfg_path(np.float32(t), g, gi, (lo, hi))

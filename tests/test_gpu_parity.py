@@ -99,6 +99,103 @@ def test_euler_edges(neo):
 
 
 # --------------------------------------------------------------------------------------
+# Classifier-free guidance fused with the Euler step
+# --------------------------------------------------------------------------------------
+
+# (cfg_scale, img_cfg_scale, interval): paths 1 (guidance off by the interval), 2 (the
+# pages' text-to-image defaults), 3 and 4
+CFG_CASES = [(4.0, 1.0, (0.95, 1.0)), (4.0, 1.0, (0.0, 1.0)), (3.0, 3.0, (0.0, 1.0)),
+             (4.0, 1.5, (0.0, 1.0))]
+
+
+@pytest.mark.parametrize("name", W.CONFIG_NAMES)
+def test_cfg_euler_configs(neo, name):
+    torch = _cuda()
+    w = W.make(name)
+    x_tu, x_u = W.cfg_branches(w)
+    t, tn = w.t_grid[0], w.t_grid[1]
+    z0 = w.z_start if w.z_start is not None else (np.float32(w.sigma_R) * w.eps_pixels)
+    z0 = z0.astype(np.float32)
+    xc_d, xtu_d, xu_d = H.dev_f32(w.x_hat), H.dev_f32(x_tu), H.dev_f32(x_u)
+    for g, gi, iv in CFG_CASES:
+        path = neo.cfg_path(t, g, gi, iv)
+        assert path == oracle.cfg_path(np.float32(t), g, gi, iv)
+        _say(f"cfg euler {name} n={z0.size} t={t}->{tn} gamma={g} gamma_img={gi} path={path}")
+        z = H.dev_f32(z0)
+        neo.fm_euler_step_cfg(z, xc_d, xtu_d, xu_d, t=t, t_next=tn, t_eps=w.t_eps,
+                              cfg_scale=g, img_cfg_scale=gi, cfg_interval=iv)
+        torch.cuda.synchronize()
+        ref = oracle.euler_step_cfg(z0, w.x_hat, x_tu, x_u, t=t, t_next=tn, t_eps=w.t_eps,
+                                    cfg_scale=g, img_cfg_scale=gi, cfg_interval=iv)
+        H.assert_close(H.host(z), ref, "f32", f"cfg euler {name} path {path}")
+
+
+def test_cfg_euler_trajectory_mid(neo):
+    """The mid workload's 20 steps with guidance on the pages' defaults (path 2) and on
+    the full three-branch path, against the oracle after every step."""
+    torch = _cuda()
+    w = W.make("mid")
+    x_tu, x_u = W.cfg_branches(w)
+    z0 = (np.float32(w.sigma_R) * w.eps_pixels).astype(np.float32)
+    xs = [H.dev_f32(a) for a in (w.x_hat, x_tu, x_u)]
+    for g, gi in ((4.0, 1.0), (4.0, 1.5)):
+        z = H.dev_f32(z0)
+        zr = z0.astype(np.float64)
+        for k in range(len(w.t_grid) - 1):
+            t, tn = w.t_grid[k], w.t_grid[k + 1]
+            _say(f"cfg trajectory gamma={g} gamma_img={gi} step {k}")
+            neo.fm_euler_step_cfg(z, *xs, t=t, t_next=tn, t_eps=w.t_eps, cfg_scale=g,
+                                  img_cfg_scale=gi)
+            zr = oracle.euler_step_cfg(zr, w.x_hat, x_tu, x_u, t=t, t_next=tn, t_eps=w.t_eps,
+                                       cfg_scale=g, img_cfg_scale=gi)
+        torch.cuda.synchronize()
+        H.assert_close(H.host(z), zr, "f32", f"cfg trajectory {g}/{gi}")
+
+
+def test_cfg_euler_edges(neo):
+    """Ragged lengths and unaligned starts (scalar path), branches the path does not read
+    passed as None, z aliasing the conditional branch, the clamp at t near 1, and n = 0;
+    path 1 matches the plain Euler kernel bit for bit."""
+    torch = _cuda()
+    rng = np.random.default_rng(9)
+    for n, off, t, tn, (g, gi) in ((1003, 0, 0.99, 1.0, (4.0, 1.5)), (4099, 1, 0.25, 0.3, (4.0, 1.0)),
+                                   (7, 3, 0.0, 0.05, (2.0, 2.0)), (64, 2, 0.5, 0.5, (4.0, 1.5))):
+        _say(f"cfg edge n={n} offset={off} gamma={g} gamma_img={gi}")
+        z0, xc, xtu, xu = (rng.standard_normal(n + off).astype(np.float32) for _ in range(4))
+        path = neo.cfg_path(t, g, gi)
+        d = [H.dev_f32(a) for a in (z0, xc, xtu, xu)]
+        args = [d[1][off:], d[2][off:] if path in (2, 4) else None,
+                d[3][off:] if path in (3, 4) else None]
+        neo.fm_euler_step_cfg(d[0][off:], *args, t=t, t_next=tn, cfg_scale=g, img_cfg_scale=gi)
+        torch.cuda.synchronize()
+        ref = oracle.euler_step_cfg(z0[off:], xc[off:], xtu[off:], xu[off:], t=t, t_next=tn,
+                                    cfg_scale=g, img_cfg_scale=gi)
+        got = H.host(d[0])
+        H.assert_close(got[off:], ref, "f32", f"cfg edge n={n} path {path}")
+        np.testing.assert_array_equal(got[:off], z0[:off])
+    # z is the conditional branch itself (read before written, element by element)
+    z0, xtu = (rng.standard_normal(513).astype(np.float32) for _ in range(2))
+    zd = H.dev_f32(z0)
+    neo.fm_euler_step_cfg(zd, zd, H.dev_f32(xtu), None, t=0.3, t_next=0.4, cfg_scale=4.0,
+                          img_cfg_scale=1.0)
+    torch.cuda.synchronize()
+    ref = oracle.euler_step_cfg(z0, z0, xtu, None, t=0.3, t_next=0.4, cfg_scale=4.0,
+                                img_cfg_scale=1.0)
+    H.assert_close(H.host(zd), ref, "f32", "cfg z aliases x0_cond")
+    # path 1 is the plain step: same bits as neo_fm_euler_step
+    z0, xc = (rng.standard_normal(4096 + 3).astype(np.float32) for _ in range(2))
+    a, b, xd = H.dev_f32(z0), H.dev_f32(z0), H.dev_f32(xc)
+    neo.fm_euler_step_cfg(a, xd, None, None, t=0.2, t_next=0.25, cfg_scale=1.0,
+                          img_cfg_scale=1.0)
+    neo.fm_euler_step(b, xd, 0.2, 0.25)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(H.host(a), H.host(b))
+    empty = torch.empty(0, device="cuda")
+    neo.fm_euler_step_cfg(empty, empty, empty, empty, t=0.1, t_next=0.2, cfg_scale=4.0,
+                          img_cfg_scale=1.5)
+
+
+# --------------------------------------------------------------------------------------
 # Norm + rotary prologue
 # --------------------------------------------------------------------------------------
 

@@ -239,3 +239,15 @@ def make(name: str, seed: int = 0, *, pixels: bool = True) -> Workload:
             # the tiny workload starts from a given z ~ N(0,1) at t = 0.6
             wl["z_start"] = wl["eps_pixels"]
     return Workload(**wl)
+
+
+def cfg_branches(w: Workload, seed: int = 0) -> tuple:
+    """x0 predictions of the two extra guidance branches (text-uncond, then full
+    uncond) for the pixel tensors of workload w: independent N(0,1) fp32 draws of the
+    same size as x_hat, from their own PCG64 stream so the workload's draws are unchanged.
+    """
+    assert w.x_hat is not None, "workload made without pixel tensors"
+    rng = np.random.default_rng([seed, 0x6366])
+    x_tu = rng.standard_normal(size=w.x_hat.size, dtype=np.float32)
+    x_u = rng.standard_normal(size=w.x_hat.size, dtype=np.float32)
+    return x_tu, x_u
