@@ -59,6 +59,9 @@ def _load():
                                         ctypes.c_double, _lp, ctypes.c_int64, _dp, _dp]
         lib.oracle_euler_step.argtypes = [_dp, _dp, ctypes.c_int64, ctypes.c_double,
                                           ctypes.c_double, ctypes.c_double]
+        lib.oracle_prefill_attn.argtypes = [_dp, _dp, _dp, _ip, _ip, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_double, _lp, ctypes.c_int64, _dp, _dp]
         lib.oracle_cfg_path.restype = ctypes.c_int
         lib.oracle_cfg_path.argtypes = [ctypes.c_double] * 5
         lib.oracle_euler_step_cfg.argtypes = [_dp, _dp, _dp, _dp, ctypes.c_int64] + [ctypes.c_double] * 7
@@ -195,3 +198,32 @@ def euler_step_cfg(z, x0_cond, x0_text_uncond=None, x0_uncond=None, *, t, t_next
         _ptr(xu, _dp) if xu is not None else None, z.size, float(t), float(t_next), float(t_eps),
         float(cfg_scale), float(img_cfg_scale), float(cfg_interval[0]), float(cfg_interval[1]))
     return z
+
+
+def prefill_attn(q, k, v, idx, cu, scale=None, tokens=None, with_lse=False):
+    """Understanding-pass attention with the block-causal mask; [A] §Block-causal
+    attention: key j is allowed for query i when idx[j] == idx[i] or j <= i.
+
+    q: [T, Hq, D]; k/v: [T, Hkv, D]; idx: [T] temporal index; cu: [B+1].
+    tokens: optional global query rows to evaluate.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    idx, cu = _i32(idx), _i32(cu)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    B = cu.shape[0] - 1
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    if tokens is None:
+        n, tok_ptr = T, None
+    else:
+        tok_arr = np.ascontiguousarray(tokens, dtype=np.int64)
+        n = tok_arr.shape[0]
+        tok_ptr = _ptr(tok_arr, _lp)
+    out = np.zeros((max(n, 1), Hq, D))
+    lse = np.zeros((max(n, 1), Hq))
+    _load().oracle_prefill_attn(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(idx, _ip),
+                                _ptr(cu, _ip), B, Hq, Hkv, D, float(scale), tok_ptr, n,
+                                _ptr(out, _dp), _ptr(lse, _dp))
+    out, lse = out[:n], lse[:n]
+    return (out, lse) if with_lse else out

@@ -271,3 +271,73 @@ void oracle_euler_step_cfg(double *z, const double *x0_c, const double *x0_tu,
         z[i] = z[i] + (t_next - t) * v;
     }
 }
+
+/*
+ * Understanding-pass (prefill) attention with the block-causal mask,
+ * [A] §Block-causal attention: within one sample, query i may attend key j
+ * when their temporal indices are equal or j <= i, i.e.
+ *     allowed(i, j) = (idx[j] == idx[i]) || (j <= i),
+ * evaluated literally for every pair (tokens sharing an index see each other
+ * both ways; across different indices the mask is causal).  Q, K and V all
+ * come from the same sequence; ragged samples by cu[B+1]; query head h reads
+ * KV head h / (Hq / Hkv); scale multiplies q.k.  Softmax in two passes (max,
+ * then exp and sum) over the allowed keys only.  Optional `tokens` selects
+ * global query rows.
+ */
+void oracle_prefill_attn(const double *q, const double *k, const double *v,
+                         const int32_t *idx, const int32_t *cu, int32_t B, int32_t Hq,
+                         int32_t Hkv, int32_t D, double scale, const int64_t *tokens,
+                         int64_t ntok, double *out, double *lse)
+{
+    const int32_t G = Hq / Hkv;
+    int64_t n = tokens ? ntok : (int64_t)cu[B];
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t job = 0; job < n * Hq; ++job) {
+        int64_t r = job / Hq;
+        int32_t h = (int32_t)(job % Hq);
+        int64_t tok = tokens ? tokens[r] : r;
+        int32_t b = 0;
+        while (b + 1 < B && tok >= cu[b + 1])
+            ++b;
+        int64_t s0 = cu[b], ns = cu[b + 1] - cu[b];
+        int64_t i = tok - s0; /* position inside the sample */
+        int32_t g = h / G;
+        const double *qr = q + (tok * Hq + h) * D;
+        double *s = (double *)malloc(sizeof(double) * (size_t)(ns > 0 ? ns : 1));
+        double m = -INFINITY;
+        for (int64_t j = 0; j < ns; ++j) {
+            int allowed = idx[s0 + j] == idx[s0 + i] || j <= i;
+            if (!allowed) {
+                s[j] = -INFINITY;
+                continue;
+            }
+            const double *kr = k + ((s0 + j) * Hkv + g) * D;
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d)
+                dot += qr[d] * kr[d];
+            s[j] = scale * dot;
+            if (s[j] > m)
+                m = s[j];
+        }
+        double denom = 0.0;
+        for (int64_t j = 0; j < ns; ++j) {
+            s[j] = s[j] == -INFINITY ? 0.0 : exp(s[j] - m);
+            denom += s[j];
+        }
+        double *o = out + (r * Hq + h) * D;
+        for (int d = 0; d < D; ++d)
+            o[d] = 0.0;
+        for (int64_t j = 0; j < ns; ++j) {
+            if (s[j] == 0.0)
+                continue;
+            const double *vr = v + ((s0 + j) * Hkv + g) * D;
+            for (int d = 0; d < D; ++d)
+                o[d] += s[j] * vr[d];
+        }
+        for (int d = 0; d < D; ++d)
+            o[d] /= denom;
+        if (lse)
+            lse[r * Hq + h] = m + log(denom);
+        free(s);
+    }
+}

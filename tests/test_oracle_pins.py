@@ -438,3 +438,94 @@ def test_cfg_missing_branch_is_an_error():
     # path 1 reads the conditional branch only
     assert oracle.euler_step_cfg([0.0], [1.0], None, None, t=0.5, t_next=0.75, cfg_scale=1.0,
                                  img_cfg_scale=1.0)[0] == 0.5
+
+
+# --------------------------------------------------------------------------------------
+# Understanding-pass attention with the block-causal mask: [A] §Block-causal attention
+# --------------------------------------------------------------------------------------
+
+def _by_key_sets(q, k, v, cu, key_sets):
+    """Reference by reduction: each query row through the (separately pinned) unmasked
+    attention oracle with exactly its allowed keys -- its own key as the one-token image
+    block, the others as the prefix."""
+    T, Hq, D = q.shape
+    out = np.zeros((T, Hq, D))
+    for i in range(T):
+        others = [j for j in key_sets[i] if j != i]
+        assert i in key_sets[i]
+        kp = k[others] if others else np.zeros((0,) + k.shape[1:])
+        vp = v[others] if others else np.zeros((0,) + v.shape[1:])
+        out[i] = oracle.gen_attn(q[i:i + 1], k[i:i + 1], v[i:i + 1], kp, vp, [0, 1],
+                                 [0, len(others)])[0]
+    return out
+
+
+def _qkv(T, Hq, Hkv, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((T, Hq, 128)), rng.standard_normal((T, Hkv, 128)),
+            rng.standard_normal((T, Hkv, 128)))
+
+
+def test_prefill_pure_text_is_causal():
+    """The pages: with every index distinct (pure text) the mask is plain causal."""
+    T = 9
+    q, k, v = _qkv(T, 4, 2, 1)
+    idx = np.arange(T) + 3
+    got = oracle.prefill_attn(q, k, v, idx, [0, T])
+    ref = _by_key_sets(q, k, v, [0, T], [list(range(i + 1)) for i in range(T)])
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_prefill_one_image_block_is_bidirectional():
+    """Tokens sharing one temporal index see each other both ways: a sample that is one
+    image block is full (unmasked) attention."""
+    T = 7
+    q, k, v = _qkv(T, 2, 1, 2)
+    got = oracle.prefill_attn(q, k, v, np.full(T, 5), [0, T])
+    ref = _by_key_sets(q, k, v, [0, T], [list(range(T))] * T)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_prefill_text_image_text_by_structure():
+    """Two ragged samples laid out text, image block (one shared index), text: text rows
+    are causal; image rows see the text before and the whole block, not the text after;
+    GQA with 2 query heads per KV head; no key crosses a sample boundary."""
+    # sample 0: 4 text, 6 image, 3 text; sample 1: 2 text, 5 image, 1 text
+    layouts = [(4, 6, 3), (2, 5, 1)]
+    idx, sets, cu = [], [], [0]
+    for (a, n, c) in layouts:
+        base = cu[-1]
+        idx += list(range(a)) + [a] * n + list(range(a + 1, a + 1 + c))
+        for i in range(a + n + c):
+            end = a + n - 1 if a <= i < a + n else i
+            sets.append([base + j for j in range(end + 1)])
+        cu.append(base + a + n + c)
+    T = cu[-1]
+    q, k, v = _qkv(T, 4, 2, 3)
+    got = oracle.prefill_attn(q, k, v, np.array(idx), cu)
+    np.testing.assert_allclose(got, _by_key_sets(q, k, v, cu, sets), rtol=0, atol=1e-12)
+
+
+def test_prefill_first_token_and_lse():
+    """A sample's first text token sees only itself: output = its v, lse = scale q.k."""
+    T = 5
+    q, k, v = _qkv(T, 2, 2, 4)
+    out, lse = oracle.prefill_attn(q, k, v, np.arange(T), [0, T], with_lse=True)
+    np.testing.assert_allclose(out[0], v[0], rtol=0, atol=1e-14)
+    for h in range(2):
+        assert lse[0, h] == pytest.approx(q[0, h] @ k[0, h] / math.sqrt(128), abs=1e-12)
+
+
+def test_prefill_block_permutation_equivariance():
+    """Inside an image block every token sees the same keys, so permuting the block's
+    tokens (q, k, v together) permutes its output rows and leaves the others unchanged."""
+    a, n, c = 3, 6, 2
+    T = a + n + c
+    idx = np.array(list(range(a)) + [a] * n + list(range(a + 1, a + 1 + c)))
+    q, k, v = _qkv(T, 2, 1, 5)
+    perm = np.arange(T)
+    perm[a:a + n] = a + np.random.default_rng(6).permutation(n)
+    o1 = oracle.prefill_attn(q, k, v, idx, [0, T])
+    o2 = oracle.prefill_attn(q[perm], k[perm], v[perm], idx, [0, T])
+    np.testing.assert_allclose(o2[a:a + n], o1[perm[a:a + n]], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o2[a + n:], o1[a + n:], rtol=0, atol=1e-12)
