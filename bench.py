@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--workload", default="large", choices=["large", "mid", "small", "editing"])
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=100,
+                    help="timed calls of the block-causal prefill attention on the editing "
+                         "workload's prefixes (0 skips it)")
     ap.add_argument("--cfg-steps", type=int, default=100,
                     help="timed calls of the guided Euler step per guidance path (0 skips it)")
     ap.add_argument("--cpu-tokens", type=int, default=256,
@@ -56,9 +59,11 @@ def parse():
 
 
 KERNELS = {"gen_attn_bf16_kernel": "gen_attn_bf16_kernel", "qknorm_rope3": "qknorm_rope3_kernel",
-           "fm_euler_step": "euler_vec4_kernel"}
+           "fm_euler_step": "euler_vec4_kernel", "prefill_attn_bf16_kernel": "prefill_attn_bf16_kernel",
+           "fm_euler_step_cfg": "euler_cfg_vec4_kernel"}
 KERNEL_SOURCES = {"gen_attn_bf16_kernel": "gen_attn.hip", "qknorm_rope3": "qknorm_rope3.hip",
-                  "fm_euler_step": "euler_step.hip"}
+                  "fm_euler_step": "euler_step.hip", "prefill_attn_bf16_kernel": "gen_attn.hip",
+                  "fm_euler_step_cfg": "euler_step.hip"}
 
 
 def _counter_rows(d, counter):
@@ -292,6 +297,45 @@ def main():
         print(f"[bench] guided Euler step timed ({a.cfg_steps} calls per path)", file=sys.stderr,
               flush=True)
 
+    # the understanding-pass (prefill) attention of the next row, on the editing workload's
+    # four ragged prefixes (text, a 1024-token reference image, suffix)
+    prefill = {}
+    if a.prefill_steps > 0:
+        we = W.make("editing", pixels=False)
+        d = W.prefill_inputs(we)
+        pq, pk, pv = (H.dev(W.bf16_round(d[x]), "bf16") for x in ("q", "k", "v"))
+        pidx, pcu = H.dev_i32(d["idx"]), H.dev_i32(d["cu"])
+        pout = torch.empty_like(pq)
+        # algorithmic work: 4*Hq*128 flops per allowed (query, key) pair
+        pairs = 0
+        for b in range(len(d["cu"]) - 1):
+            ix = d["idx"][d["cu"][b]:d["cu"][b + 1]]
+            last = np.searchsorted(ix, ix, side="right") - 1   # end of each query's index run
+            pairs += int(np.sum(np.maximum(np.arange(ix.size), last) + 1))
+        pflops = 4.0 * we.Hq * 128 * pairs
+
+        def pre_call():
+            neo.prefill_attn_fwd(pq, pk, pv, pidx, pcu, d["max_len"], out=pout)
+        for _ in range(10):
+            pre_call()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(a.prefill_steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record()
+            pre_call()
+            e1.record()
+        torch.cuda.synchronize()
+        us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
+        prefill = {"workload": (f"editing prefixes: {len(d['cu']) - 1} samples, "
+                                f"{list(np.diff(d['cu']))} tokens, Hq={we.Hq}, Hkv={we.Hkv}"),
+                   "allowed_pairs": pairs, "gflop": pflops / 1e9, "us": us,
+                   "tflops": pflops / (us * 1e-6) / 1e12,
+                   "frac": pflops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS}
+        del pq, pk, pv, pout
+        print(f"[bench] prefill attention timed ({a.prefill_steps} calls)", file=sys.stderr,
+              flush=True)
+
     cpu = None
     if not a.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
@@ -330,6 +374,7 @@ def main():
         "step_roofline": {"tokens_per_s_at_roofline": ntok / roof_step_s,
                           "frac": (ntok / gpu_step_s) / (ntok / roof_step_s)},
         "cfg_euler": cfg,
+        "prefill_attention": prefill,
     }
     print(json.dumps(result), flush=True)
 

@@ -159,6 +159,35 @@ neo_status neo_fm_euler_step(float *z, const float *x0_pred, int64_t n, float t,
                              float t_eps, void *hip_stream);
 
 /*
+ * neo_prefill_attn_fwd -- understanding-pass (prefill) attention with the
+ * block-causal mask ([A] §Block-causal attention; [B] §2.5, Fig. 6).  Within
+ * each sample, query i attends key j when temporal_idx[j] == temporal_idx[i]
+ * or j <= i: tokens sharing a temporal index (one image) see each other both
+ * ways, and across different indices the mask is causal.  This produces the
+ * frozen K/V prefix's attention outputs; Q, K and V all come from the same
+ * sequence (already normed and rotated).
+ *
+ *   q             [T, Hq, 128] bf16; k, v [T, Hkv, 128] bf16; 16-byte aligned.
+ *   temporal_idx  [T] int32, device: each token's temporal index (the first
+ *                 rotary axis).  Precondition, not checked: within a sample the
+ *                 indices are non-decreasing and tokens sharing an index are
+ *                 contiguous, as in every layout the pages describe (text
+ *                 tokens count up; an image's tokens share one index).
+ *   cu_seqlens    [B+1] int32, device: sample s is rows [cu[s], cu[s+1]).
+ *   max_seqlen    host-side bound on the sample lengths; total = T.
+ *   softmax_scale <= 0 means 1/sqrt(128).
+ *   out           [T, Hq, 128] bf16; lse optional [Hq, T] fp32 (natural log).
+ *   dtype         NEO_BF16 only (the understanding branch is bf16, [A]
+ *                 §Numeric precision); NEO_F32 -> NEO_ERR_UNSUPPORTED.
+ * Errors as for neo_gen_attn_fwd; out and lse may not overlap any input.
+ */
+neo_status neo_prefill_attn_fwd(const void *q, const void *k, const void *v,
+                                const int32_t *temporal_idx, const int32_t *cu_seqlens,
+                                int32_t B, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                                int64_t total, int32_t max_seqlen, float softmax_scale,
+                                void *out, float *lse, neo_dtype dtype, void *hip_stream);
+
+/*
  * neo_cfg_path -- which classifier-free guidance path a flow step takes
  * ([B] §2.7, the four code paths of the main loop).  Guidance is on when
  * cfg_interval_lo < t < cfg_interval_hi, or always when cfg_interval_lo == 0;

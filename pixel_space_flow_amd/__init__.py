@@ -13,7 +13,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["qknorm_rope3", "gen_attn_fwd", "fm_euler_step", "fm_euler_step_cfg", "cfg_path",
+__all__ = ["qknorm_rope3", "gen_attn_fwd", "prefill_attn_fwd", "fm_euler_step",
+           "fm_euler_step_cfg", "cfg_path",
            "NeoError", "lib", "LIB_PATH", "EXPORTED_SYMBOLS", "NEO_OK", "NEO_ERR_NULL", "NEO_ERR_SHAPE", "NEO_ERR_VALUE",
            "NEO_ERR_UNSUPPORTED", "NEO_ERR_HIP", "NEO_F32", "NEO_BF16"]
 
@@ -23,8 +24,8 @@ NEO_OK, NEO_ERR_NULL, NEO_ERR_SHAPE, NEO_ERR_VALUE, NEO_ERR_UNSUPPORTED, NEO_ERR
 NEO_F32, NEO_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = ("neo_qknorm_rope3", "neo_gen_attn_fwd", "neo_fm_euler_step",
-                    "neo_cfg_path", "neo_fm_euler_step_cfg", "neo_status_string",
-                    "neo_last_error")
+                    "neo_cfg_path", "neo_fm_euler_step_cfg", "neo_prefill_attn_fwd",
+                    "neo_status_string", "neo_last_error")
 
 _vp = ctypes.c_void_p
 _i32, _i64, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
@@ -55,6 +56,9 @@ def lib() -> ctypes.CDLL:
                                        _i64, _i64, _i32, _i32, _f32, _vp, _vp, ctypes.c_int, _vp]
         L.neo_fm_euler_step.restype = ctypes.c_int
         L.neo_fm_euler_step.argtypes = [_vp, _vp, _i64, _f32, _f32, _f32, _vp]
+        L.neo_prefill_attn_fwd.restype = ctypes.c_int
+        L.neo_prefill_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64,
+                                           _i32, _f32, _vp, _vp, ctypes.c_int, _vp]
         L.neo_cfg_path.restype = ctypes.c_int
         L.neo_cfg_path.argtypes = [_f32] * 5
         L.neo_fm_euler_step_cfg.restype = ctypes.c_int
@@ -171,6 +175,37 @@ def gen_attn_fwd(q, k_img, v_img, k_prefix, v_prefix, cu_seqlens_q, cu_seqlens_p
                                 lse.data_ptr() if lse is not None else None, _dtype_code(q),
                                 _stream(q))
     _check("neo_gen_attn_fwd", st)
+    return (out, lse) if return_lse else out
+
+
+def prefill_attn_fwd(q, k, v, temporal_idx, cu_seqlens, max_seqlen, softmax_scale=0.0, out=None,
+                     return_lse=False):
+    """Understanding-pass attention with the block-causal mask ([A] §Block-causal
+    attention): key j is open to query i when their temporal indices are equal or j <= i.
+
+    q [T, Hq, 128] bf16; k/v [T, Hkv, 128] bf16; temporal_idx int32 [T] and cu_seqlens
+    int32 [B+1] on the device (indices non-decreasing within a sample, equal ones
+    contiguous); max_seqlen a host int.  Returns out (and lse [Hq, T] if return_lse).
+    """
+    torch = _torch()
+    _dev(q, "q")
+    T, Hq, D = q.shape
+    _dev(k, "k", q.dtype)
+    _dev(v, "v", q.dtype, k.shape)
+    if k.dim() != 3 or k.shape[0] != T:
+        raise ValueError("k must be [T, Hkv, 128]")
+    Hkv = k.shape[1]
+    _dev(temporal_idx, "temporal_idx", torch.int32, (T,))
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    B = cu_seqlens.shape[0] - 1
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype, q.shape)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device) if return_lse else None
+    st = lib().neo_prefill_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                    temporal_idx.data_ptr(), cu_seqlens.data_ptr(), B, Hq, Hkv,
+                                    D, T, int(max_seqlen), float(softmax_scale), out.data_ptr(),
+                                    lse.data_ptr() if lse is not None else None, _dtype_code(q),
+                                    _stream(q))
+    _check("neo_prefill_attn_fwd", st)
     return (out, lse) if return_lse else out
 
 

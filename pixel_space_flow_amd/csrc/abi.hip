@@ -202,6 +202,62 @@ neo_status neo_fm_euler_step(float* z, const float* x0_pred, int64_t n, float t,
                   "neo_fm_euler_step launch");
 }
 
+neo_status neo_prefill_attn_fwd(const void* q, const void* k, const void* v,
+                                const int32_t* temporal_idx, const int32_t* cu_seqlens,
+                                int32_t B, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                                int64_t total, int32_t max_seqlen, float softmax_scale,
+                                void* out, float* lse, neo_dtype dtype, void* hip_stream) {
+  const char* fn = "neo_prefill_attn_fwd";
+  if (dtype != NEO_F32 && dtype != NEO_BF16)
+    return fail(NEO_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, (int)dtype);
+  if (dtype != NEO_BF16)
+    return fail(NEO_ERR_UNSUPPORTED, "%s: the understanding pass is bf16 only", fn);
+  if (head_dim != NEO_HEAD_DIM)
+    return fail(NEO_ERR_SHAPE, "%s: head_dim must be 128, got %d", fn, head_dim);
+  if (B < 1 || Hq < 1 || Hkv < 1)
+    return fail(NEO_ERR_SHAPE, "%s: B=%d Hq=%d Hkv=%d must be >= 1", fn, B, Hq, Hkv);
+  if (Hq % Hkv != 0)
+    return fail(NEO_ERR_SHAPE, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
+  if (max_seqlen < 0) return fail(NEO_ERR_SHAPE, "%s: negative max_seqlen", fn);
+  if (!rows_fit(total, Hq))
+    return fail(NEO_ERR_SHAPE, "%s: total=%lld out of range", fn, (long long)total);
+  if (max_seqlen > total) return fail(NEO_ERR_SHAPE, "%s: max_seqlen exceeds the tensor's rows", fn);
+  if ((int64_t)max_seqlen * Hkv * NEO_HEAD_DIM * 4 >= ((int64_t)1 << 31))
+    return fail(NEO_ERR_SHAPE, "%s: one sample's K/V rows exceed 2 GiB", fn);
+  if (!isfinite(softmax_scale)) return fail(NEO_ERR_VALUE, "%s: softmax_scale must be finite", fn);
+  {
+    const int64_t G = Hq / Hkv;
+    const int64_t per = ((int64_t)G * ((max_seqlen + 31) / 32) + 7) / 8;
+    if (per * Hkv * B >= ((int64_t)1 << 31))
+      return fail(NEO_ERR_SHAPE, "%s: problem too large for one launch", fn);
+  }
+  if (max_seqlen == 0 || total == 0) return ok();
+  if (!q || !k || !v || !temporal_idx || !cu_seqlens || !out)
+    return fail(NEO_ERR_NULL, "%s: a required pointer is NULL", fn);
+  const void* bufs[3] = {q, k, v};
+  for (const void* p : bufs)
+    if (!aligned16(p)) return fail(NEO_ERR_VALUE, "%s: q/k/v buffers must be 16-byte aligned", fn);
+  if (!aligned16(out)) return fail(NEO_ERR_VALUE, "%s: out must be 16-byte aligned", fn);
+  if (reinterpret_cast<uintptr_t>(temporal_idx) & 3)
+    return fail(NEO_ERR_VALUE, "%s: temporal_idx must be 4-byte aligned", fn);
+  const size_t ob = (size_t)total * Hq * NEO_HEAD_DIM * 2;
+  const size_t kb = (size_t)total * Hkv * NEO_HEAD_DIM * 2;
+  const size_t sizes[3] = {ob, kb, kb};
+  const size_t lb = lse ? (size_t)total * Hq * sizeof(float) : 0;
+  for (int i = 0; i < 3; ++i)
+    if (overlap(out, ob, bufs[i], sizes[i]) || (lse && overlap(lse, lb, bufs[i], sizes[i])))
+      return fail(NEO_ERR_VALUE, "%s: out/lse overlap an input", fn);
+  if (lse && overlap(lse, lb, out, ob)) return fail(NEO_ERR_VALUE, "%s: lse overlaps out", fn);
+  if (overlap(out, ob, temporal_idx, (size_t)total * 4) ||
+      (lse && overlap(lse, lb, temporal_idx, (size_t)total * 4)))
+    return fail(NEO_ERR_VALUE, "%s: out/lse overlap temporal_idx", fn);
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)NEO_HEAD_DIM);
+  return from_hip(neo::launch_prefill_attn_bf16(q, k, v, temporal_idx, cu_seqlens, B, Hq, Hkv,
+                                                max_seqlen, scale, out, lse, total,
+                                                static_cast<hipStream_t>(hip_stream)),
+                  "neo_prefill_attn_fwd launch");
+}
+
 int neo_cfg_path(float t, float cfg_scale, float img_cfg_scale, float cfg_interval_lo,
                  float cfg_interval_hi) {
   // the pages' loop: guidance on strictly inside the interval, or always when the

@@ -122,13 +122,38 @@ __device__ __forceinline__ int sub_valid(const Segments& S, int s) {
   return (pre ? S.len[0] : S.len[1]) - tl * kBN - (s & 1) * 32;
 }
 
-__global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
+// Last position of the run of equal temporal indices that contains position `start`
+// (within a sample the indices are non-decreasing and equal ones are contiguous).  All
+// lanes of the wave call it with the same arguments; 64 positions per probe.
+__device__ __forceinline__ int run_end(const int32_t* ix, int start, int n, int lane) {
+  const int v0 = ix[start];
+  for (int base = start + 1; base < n; base += 64) {
+    const int p = base + lane;
+    const bool differs = p >= n || ix[p] != v0;  // no read at or past n
+    const uint64_t bal = __ballot(differs);
+    if (bal != 0) return base + (int)__builtin_ctzll(bal) - 1;
+  }
+  return n - 1;
+}
+
+// The bf16 attention body.  kPrefill = false: the generation pass (image queries over
+// [prefix ; image block], unmasked).  kPrefill = true: the understanding pass over one
+// sequence with the block-causal mask ("SenseNova-U1.5 (NEO-unify) architecture",
+// §Block-causal attention: key j is open to query i when their temporal indices are
+// equal or j <= i).  With a sample's indices non-decreasing and equal indices contiguous,
+// query i sees exactly the keys 0 .. end(i), end(i) = max(i, last position of its index
+// run); the prefill variant runs the same pipeline with no prefix segment, the key range
+// of a workgroup cut at end() of its last query, and each lane masking keys past its own
+// end().  ("SenseNova-U1 ... NEO-unify Architecture" paper notes, §2.5, Fig. 6: image
+// query blocks extend the key range, text blocks stay causal.)
+template <bool kPrefill>
+__device__ __forceinline__ void attn_bf16_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_img,
     const uint16_t* __restrict__ v_img, const uint16_t* __restrict__ k_pre,
     const uint16_t* __restrict__ v_pre, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ cu_p, int Hq, int Hkv, int n_cg, int max_q, int max_p,
-    int64_t Tq, int64_t Tp, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse) {
+    const int32_t* __restrict__ cu_p, const int32_t* __restrict__ tidx, int Hq, int Hkv,
+    int n_cg, int max_q, int max_p, int64_t Tq, int64_t Tp, float scale_log2,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
   // six separate LDS objects, so the compiler sees that a tile load into one buffer
   // cannot alias fragment reads from another and does not wait for it
   __shared__ __attribute__((aligned(1024))) uint8_t lk0[kTileBytes], lk1[kTileBytes],
@@ -141,7 +166,9 @@ __global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
   };
 
   const uint32_t id = xcd_remap(blockIdx.x, gridDim.x);
-  const int cg = (int)(id % (uint32_t)n_cg);
+  // prefill: the heaviest workgroups (latest queries, longest key ranges) start first
+  const int cg0 = (int)(id % (uint32_t)n_cg);
+  const int cg = kPrefill ? n_cg - 1 - cg0 : cg0;
   const int rest = (int)(id / (uint32_t)n_cg);
   const int g = rest % Hkv;
   const int b = rest / Hkv;
@@ -154,7 +181,7 @@ __global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
   pa = pa < 0 ? 0 : (pa > Tp ? Tp : pa);
   pb_ = pb_ < pa ? pa : (pb_ > Tp ? Tp : pb_);
   const int N = (int)((qb - qa) < max_q ? (qb - qa) : max_q);
-  const int P = (int)((pb_ - pa) < max_p ? (pb_ - pa) : max_p);
+  const int P = kPrefill ? 0 : (int)((pb_ - pa) < max_p ? (pb_ - pa) : max_p);
 
   const int G = Hq / Hkv;
   const int nchunks = G * ((N + 31) / 32);
@@ -168,6 +195,30 @@ __global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
   const int qi = (active ? c / G : 0) * 32 + col;  // query index inside the sample
   const bool qvalid = active && qi < N;
 
+  // prefill: the keys the workgroup's queries may see are 0 .. kmax-1; lane_lim is the
+  // number of keys this lane's query may see, lim_min the smallest over the wave
+  int kmax = N, lane_lim = 1 << 30, lim_min = 1 << 30;
+  if constexpr (kPrefill) {
+    const int32_t* ix = tidx + qa;
+    const int last_c = (cg * kWaves + kWaves < nchunks ? cg * kWaves + kWaves : nchunks) - 1;
+    const int wg_last = ((last_c / G) * 32 + 32 < N ? (last_c / G) * 32 + 32 : N) - 1;
+    kmax = run_end(ix, wg_last, N, lane) + 1;
+    if (active) {
+      const int t0 = (c / G) * 32;
+      const int nq = N - t0 < 32 ? N - t0 : 32;
+      const int my = qvalid ? ix[qi] : 0;
+      int e = col;  // last query of the wave in this lane's run
+      for (int m = 1; m < 32; ++m) {
+        const int im = __shfl(my, m);
+        if (m > col && m < nq && e == m - 1 && im == my) e = m;
+      }
+      const int wave_end = run_end(ix, t0 + nq - 1, N, lane);
+      lane_lim = (e == nq - 1 ? wave_end : t0 + e) + 1;
+      if (!qvalid) lane_lim = kmax;
+      lim_min = __shfl(lane_lim, 0);
+    }
+  }
+
   Segments S;
   S.row_bytes = (uint32_t)Hkv * kHeadDim * 2;
   S.tile_bytes = S.row_bytes * kBN;
@@ -176,9 +227,9 @@ __global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
   S.kbase[1] = reinterpret_cast<const uint8_t*>(k_img + (qa * Hkv + g) * kHeadDim);
   S.vbase[1] = reinterpret_cast<const uint8_t*>(v_img + (qa * Hkv + g) * kHeadDim);
   S.len[0] = P;
-  S.len[1] = N;
+  S.len[1] = kmax;
   S.ntiles[0] = (P + kBN - 1) / kBN;
-  S.ntiles[1] = (N + kBN - 1) / kBN;
+  S.ntiles[1] = (kmax + kBN - 1) / kBN;
   const int ntiles = S.ntiles[0] + S.ntiles[1];
   const int nsub = 2 * ntiles;  // 32-key sub-tiles (trailing ones may be fully masked)
 
@@ -268,11 +319,15 @@ __global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
   };
 
   // keys of sub-tile s past its segment's end score -inf
+  // (prefill: also keys past this lane's own end; sub-tile s starts at key 32*s there)
   auto mask = [&](int s, f32x16& sacc) {
     const int nvalid = sub_valid(S, s);
-    if (nvalid < 32) {
+    const bool edge = kPrefill ? (nvalid < 32 || 32 * s + 32 > lim_min) : nvalid < 32;
+    if (edge) {
       // key = (r/4)*8 + hl*4 + r%4; compare its constant part with one limit
-      const int lim = nvalid - hl * 4;
+      int lim = nvalid;
+      if (kPrefill) lim = lane_lim - 32 * s < lim ? lane_lim - 32 * s : lim;
+      lim -= hl * 4;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if ((r >> 2) * 8 + (r & 3) >= lim) sacc[r] = -INFINITY;
@@ -443,6 +498,26 @@ __global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
   }
 }
 
+__global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_img,
+    const uint16_t* __restrict__ v_img, const uint16_t* __restrict__ k_pre,
+    const uint16_t* __restrict__ v_pre, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_p, int Hq, int Hkv, int n_cg, int max_q, int max_p,
+    int64_t Tq, int64_t Tp, float scale_log2, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
+  attn_bf16_body<false>(q, k_img, v_img, k_pre, v_pre, cu_q, cu_p, nullptr, Hq, Hkv, n_cg, max_q,
+                        max_p, Tq, Tp, scale_log2, out, lse);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void prefill_attn_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ tidx, int Hq, int Hkv, int n_cg, int max_len, int64_t T,
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  attn_bf16_body<true>(q, k, v, k, v, cu, cu, tidx, Hq, Hkv, n_cg, max_len, 0, T, T,
+                       scale_log2, out, lse);
+}
+
 // ---------------------------------------------------------------------------------------
 // fp32 path
 // ---------------------------------------------------------------------------------------
@@ -560,6 +635,23 @@ hipError_t launch_gen_attn_bf16(const void* q, const void* k_img, const void* v_
                      static_cast<const uint16_t*>(v_img), static_cast<const uint16_t*>(k_pre),
                      static_cast<const uint16_t*>(v_pre), cu_q, cu_p, Hq, Hkv, (int)n_cg,
                      max_q, max_p, Tq, Tp, scale_log2, static_cast<uint16_t*>(out), lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_attn_bf16(const void* q, const void* k, const void* v,
+                                    const int32_t* tidx, const int32_t* cu, int B, int Hq,
+                                    int Hkv, int max_len, float scale, void* out, float* lse,
+                                    int64_t T, hipStream_t stream) {
+  if (max_len == 0 || T == 0) return hipSuccess;
+  const int G = Hq / Hkv;
+  const int64_t chunks = (int64_t)G * ((max_len + 31) / 32);
+  const int64_t n_cg = (chunks + kWaves - 1) / kWaves;
+  const int64_t blocks = n_cg * Hkv * B;
+  const float scale_log2 = (float)((double)scale * 1.4426950408889634073599246810019);
+  hipLaunchKernelGGL(prefill_attn_bf16_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), cu, tidx, Hq, Hkv, (int)n_cg, max_len, T,
+                     scale_log2, static_cast<uint16_t*>(out), lse);
   return hipGetLastError();
 }
 

@@ -24,6 +24,11 @@ hipError_t launch_gen_attn_bf16(const void* q, const void* k_img, const void* v_
                                 int max_p, float scale, void* out, float* lse, int64_t Tq,
                                 int64_t Tp, hipStream_t stream);
 
+hipError_t launch_prefill_attn_bf16(const void* q, const void* k, const void* v,
+                                    const int32_t* tidx, const int32_t* cu, int B, int Hq,
+                                    int Hkv, int max_len, float scale, void* out, float* lse,
+                                    int64_t T, hipStream_t stream);
+
 hipError_t launch_gen_attn_f32(const float* q, const float* k_img, const float* v_img,
                                const float* k_pre, const float* v_pre, const int32_t* cu_q,
                                const int32_t* cu_p, int B, int Hq, int Hkv, int max_q, int max_p,

@@ -203,3 +203,39 @@ def test_cfg_path_matches_the_oracle_rule():
                       float(rng.choice([1.0, 0.75]))))
     for t, g, gi, lo, hi in cases:
         assert P.cfg_path(t, g, gi, (lo, hi)) == oracle.cfg_path(np.float32(t), g, gi, (lo, hi))
+
+
+def _pre(L, **kw):
+    a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), ti=W, cu=W + 256, B=1, Hq=32, Hkv=8,
+             D=128, T=1500, mx=1500, scale=0.0, out=FAKE + (3 << 30), lse=None,
+             dtype=P.NEO_BF16)
+    a.update(kw)
+    return L.neo_prefill_attn_fwd(a["q"], a["k"], a["v"], a["ti"], a["cu"], a["B"], a["Hq"],
+                                  a["Hkv"], a["D"], a["T"], a["mx"], a["scale"], a["out"],
+                                  a["lse"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=P.NEO_F32), P.NEO_ERR_UNSUPPORTED),             # the understanding pass is bf16
+    (dict(dtype=5), P.NEO_ERR_UNSUPPORTED),
+    (dict(D=64), P.NEO_ERR_SHAPE),
+    (dict(Hkv=5), P.NEO_ERR_SHAPE),
+    (dict(mx=1501), P.NEO_ERR_SHAPE),
+    (dict(B=0), P.NEO_ERR_SHAPE),
+    (dict(scale=math.nan), P.NEO_ERR_VALUE),
+    (dict(ti=None), P.NEO_ERR_NULL),
+    (dict(cu=None), P.NEO_ERR_NULL),
+    (dict(k=FAKE + (1 << 30) + 8), P.NEO_ERR_VALUE),             # misaligned
+    (dict(ti=W + 2), P.NEO_ERR_VALUE),                           # misaligned indices
+    (dict(out=FAKE + (2 << 30)), P.NEO_ERR_VALUE),              # out aliases v
+    (dict(lse=FAKE + (3 << 30) + 4096), P.NEO_ERR_VALUE),       # lse inside out
+    (dict(T=1 << 21, mx=1 << 21), P.NEO_ERR_SHAPE),             # one sample's K/V beyond 2 GiB
+])
+def test_prefill_validation(L, kw, status):
+    assert _pre(L, **kw) == status
+    assert L.neo_last_error().decode().startswith("neo_prefill_attn_fwd")
+
+
+def test_prefill_empty_is_ok(L):
+    assert _pre(L, mx=0, q=None) == P.NEO_OK
+    assert _pre(L, T=0, mx=0) == P.NEO_OK

@@ -429,3 +429,75 @@ def test_block_end_to_end(neo, name):
     ref = oracle.gen_attn(qr, kr, w.v, kp, vp, w.cu_q, w.cu_p, tokens=rows)
     got = H.host(out) if rows is None else H.host(out)[rows]
     H.assert_close(got, ref, d, f"block {name}")
+
+
+# --------------------------------------------------------------------------------------
+# Understanding-pass attention with the block-causal mask
+# --------------------------------------------------------------------------------------
+
+def _prefill_case(neo, d, what, rows=None, lse=True):
+    torch = _cuda()
+    qb, kb, vb = (W.bf16_round(d[x]) for x in ("q", "k", "v"))
+    _say(f"prefill {what}: T={qb.shape[0]} Hq={qb.shape[1]} Hkv={kb.shape[1]} "
+         f"cu={list(d['cu'])[:6]}")
+    out, lse_d = neo.prefill_attn_fwd(H.dev(qb, "bf16"), H.dev(kb, "bf16"), H.dev(vb, "bf16"),
+                                      H.dev_i32(d["idx"]), H.dev_i32(d["cu"]), d["max_len"],
+                                      return_lse=True)
+    torch.cuda.synchronize()
+    got = H.host(out)
+    ref, ref_lse = oracle.prefill_attn(qb, kb, vb, d["idx"], d["cu"], tokens=rows, with_lse=True)
+    if rows is not None:
+        got = got[rows]
+    H.assert_close(got, ref, "bf16", f"prefill {what}")
+    if lse:
+        gl = H.host(lse_d).T
+        gl = gl[rows] if rows is not None else gl
+        assert np.max(np.abs(gl - ref_lse)) < 2e-2, f"prefill {what}: lse"
+
+
+@pytest.mark.parametrize("name", W.CONFIG_NAMES)
+def test_prefill_configs(neo, name):
+    """Each workload's prefix through the prefill attention: pure text (causal) for all but
+    the editing workload, whose four ragged prefixes hold a 1024-token reference image
+    between text and suffix; the editing case is compared on sampled rows (first, last and
+    around every run boundary of each sample, plus a stride)."""
+    w = W.make(name, pixels=False)
+    d = W.prefill_inputs(w)
+    rows = None
+    if name == "editing":
+        sel = set(range(0, d["cu"][-1], 37))
+        for b in range(len(d["cu"]) - 1):
+            a, e = d["cu"][b], d["cu"][b + 1]
+            ix = d["idx"][a:e]
+            cuts = np.nonzero(np.diff(ix))[0]
+            for cpos in list(cuts) + [0, e - a - 1]:
+                sel.update(a + j for j in range(cpos - 2, cpos + 3) if 0 <= j < e - a)
+        rows = np.array(sorted(sel))
+    _prefill_case(neo, d, name, rows)
+
+
+PREFILL_LAYOUTS = {
+    # a run crossing 32-token wave and 64-token workgroup boundaries
+    "text20_img50_text30": [[("text", 20), ("image", 50), ("text", 30)]],
+    # one sample that is one image block (bidirectional), one shorter than a wave
+    "image_only_and_short": [[("image", 150)], [("text", 5)]],
+    # a run ending exactly at a wave boundary and another starting at one
+    "aligned_runs": [[("text", 32), ("image", 32), ("image", 64), ("text", 1)]],
+    # ragged batch, single-token sample, text-only sample with a ragged tail
+    "ragged": [[("text", 1)], [("text", 97)], [("text", 3), ("image", 200), ("text", 10)]],
+    # an image run that starts in one workgroup's last wave and runs 300 tokens on
+    "long_run": [[("text", 60), ("image", 300), ("text", 70)]],
+}
+
+
+@pytest.mark.parametrize("layout", sorted(PREFILL_LAYOUTS))
+def test_prefill_layouts(neo, layout):
+    d = W.prefill_layout(PREFILL_LAYOUTS[layout], 32, 8, seed=len(layout))
+    _prefill_case(neo, d, layout)
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (32, 4), (12, 4)])
+def test_prefill_heads(neo, hq, hkv):
+    d = W.prefill_layout([[("text", 40), ("image", 70), ("text", 9)], [("text", 33)]], hq, hkv,
+                         seed=hq * 10 + hkv)
+    _prefill_case(neo, d, f"Hq={hq} Hkv={hkv}")

@@ -251,3 +251,47 @@ def cfg_branches(w: Workload, seed: int = 0) -> tuple:
     x_tu = rng.standard_normal(size=w.x_hat.size, dtype=np.float32)
     x_u = rng.standard_normal(size=w.x_hat.size, dtype=np.float32)
     return x_tu, x_u
+
+
+def prefill_inputs(w: Workload, seed: int = 0) -> dict:
+    """Inputs of the understanding-pass (prefill) attention over workload w's prefix
+    tokens: the temporal index of every prefix token (its layout's first rotary axis when
+    the workload builds the prefix by structure; 0..P_b-1, pure text, when the workload
+    draws the frozen cache directly), and Q [Tp, Hq, 128], K and V [Tp, Hkv, 128] as
+    N(0,1) fp32 draws from their own PCG64 stream (q, then k, then v)."""
+    rng = np.random.default_rng([seed, 0x7066])
+    Tp = int(w.cu_p[-1])
+    if w.pos_prefix is not None:
+        idx = np.ascontiguousarray(w.pos_prefix[0], dtype=np.int32)
+    else:
+        idx = np.concatenate([np.arange(p, dtype=np.int32) for p in w.n_prefix])
+    q = rng.standard_normal(size=(Tp, w.Hq, 128), dtype=np.float32)
+    k = rng.standard_normal(size=(Tp, w.Hkv, 128), dtype=np.float32)
+    v = rng.standard_normal(size=(Tp, w.Hkv, 128), dtype=np.float32)
+    return {"q": q, "k": k, "v": v, "idx": idx, "cu": np.asarray(w.cu_p, dtype=np.int32),
+            "max_len": int(max(w.n_prefix))}
+
+
+def prefill_layout(segments, Hq: int, Hkv: int, seed: int = 0) -> dict:
+    """A hand-made prefill case: `segments` lists, per sample, runs of ("text", n) or
+    ("image", n); text tokens take consecutive temporal indices, an image's n tokens share
+    the next one.  Q/K/V are N(0,1) fp32 draws as in prefill_inputs."""
+    rng = np.random.default_rng([seed, 0x706c])
+    idx, cu = [], [0]
+    for sample in segments:
+        t = 0
+        for kind, n in sample:
+            if kind == "text":
+                idx += list(range(t, t + n))
+                t += n
+            else:
+                idx += [t] * n
+                t += 1
+        cu.append(len(idx))
+    T = len(idx)
+    q = rng.standard_normal(size=(T, Hq, 128), dtype=np.float32)
+    k = rng.standard_normal(size=(T, Hkv, 128), dtype=np.float32)
+    v = rng.standard_normal(size=(T, Hkv, 128), dtype=np.float32)
+    lens = np.diff(cu)
+    return {"q": q, "k": k, "v": v, "idx": np.asarray(idx, dtype=np.int32),
+            "cu": np.asarray(cu, dtype=np.int32), "max_len": int(lens.max()) if len(lens) else 0}
