@@ -67,6 +67,7 @@ constexpr float kTwoTau = 256.0f;            // bound on any softmax weight (2^8
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 constexpr int kBufFlags = 0x00020000;        // raw buffer, 32-bit data format (gfx9 family)
 constexpr int kPrefetch = 3;                 // slots of LDS operands read ahead (<= 3)
+constexpr int kLoadSlotK = 1, kLoadSlotV = 3;  // slots that issue the next tiles' loads
 
 // LDS tiles hold 64 rows of 16 chunks (16 bytes = 8 dims each).  Chunk c of row r is
 // stored at slot c ^ swz(r), which keeps the K-fragment reads (16 consecutive rows, one
@@ -395,7 +396,6 @@ __device__ __forceinline__ void attn_bf16_body(
     mask(s + 1, snext);
   };
 
-
   // prologue: K tiles 0 and 1, V tile 0; V buffer 2 cleared (the first step's PV
   // product reads it against an all-zero P); scores of sub-tile 0
   load_k(0, 0);
@@ -429,9 +429,10 @@ __device__ __forceinline__ void attn_bf16_body(
     constexpr int T3 = decltype(t3)::value;
     constexpr int b0 = T3, b1 = (T3 + 1) % 3, bm1 = (T3 + 2) % 3;
     const bool kmore = T + 2 < ntiles, vmore = T + 1 < ntiles;
-    if (kmore) load_k(T + 2, bm1);
-    if (vmore) load_v(T + 1, b1);
-    if (active) {
+    if (!active) {
+      if (kmore) load_k(T + 2, bm1);
+      if (vmore) load_v(T + 1, b1);
+    } else {
       uint32_t pk[2][4];
       float tsum = 0.0f;
 #pragma unroll
@@ -454,6 +455,10 @@ __device__ __forceinline__ void attn_bf16_body(
         snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k & 3], qf[i], i == 0 ? zero16 : snext,
                                                         0, 0, 0);
         o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[k & 3], pprev[i >> 2], o[i & 3], 0, 0, 0);
+        // the next tiles' loads (scalar descriptor set-up, then LDS-direct loads) go under
+        // the matrix products of early slots rather than right after the barrier
+        if (k == kLoadSlotK && kmore) load_k(T + 2, bm1);
+        if (k == kLoadSlotV && vmore) load_v(T + 1, b1);
         exp_pair(scur, i, pk, tsum);
         __builtin_amdgcn_sched_barrier(0);
         if (i == 7) finish_step(2 * T + h, scur, snext, pcur, pk, tsum);
