@@ -227,3 +227,29 @@ def prefill_attn(q, k, v, idx, cu, scale=None, tokens=None, with_lse=False):
                                 _ptr(out, _dp), _ptr(lse, _dp))
     out, lse = out[:n], lse[:n]
     return (out, lse) if with_lse else out
+
+
+def qkv_proj_norm_rope(x, w_qkv, Hq, Hkv, wq_t, wq_hw, wk_t, wk_hw, pos, theta=5.0e6,
+                       theta_hw=1.0e4, eps=1e-6, tokens=None):
+    """The generation branch's q/k/v projection followed by the q/k prologue; [A] §Mixture
+    of Transformers (the `_mot_gen` q/k/v projections and q/k norms) and §Three rotary axes.
+
+    x [N, hidden]; w_qkv [(Hq + 2 Hkv) * 128, hidden], rows: the Hq query heads, then the Hkv
+    key heads, then the Hkv value heads (y = x w_qkv^T).  pos [3, N].  The projection is an
+    fp64 library matmul; q and k then go through norm_rope (split-half RMSNorm + three-axis
+    rotary); v is the projection itself.  tokens: optional rows to evaluate.
+    Returns (q [n, Hq, 128], k [n, Hkv, 128], v [n, Hkv, 128]).
+    """
+    x, w = _f64(x), _f64(w_qkv)
+    pos = _i32(pos)
+    if tokens is not None:
+        tokens = np.asarray(tokens, dtype=np.int64)
+        x, pos = x[tokens], np.ascontiguousarray(pos[:, tokens])
+    n = x.shape[0]
+    assert w.shape == ((Hq + 2 * Hkv) * 128, x.shape[1])
+    y = x @ w.T
+    q = np.ascontiguousarray(y[:, :Hq * 128]).reshape(n, Hq, 128)
+    k = np.ascontiguousarray(y[:, Hq * 128:(Hq + Hkv) * 128]).reshape(n, Hkv, 128)
+    v = np.ascontiguousarray(y[:, (Hq + Hkv) * 128:]).reshape(n, Hkv, 128)
+    return (norm_rope(q, wq_t, wq_hw, pos, theta, theta_hw, eps),
+            norm_rope(k, wk_t, wk_hw, pos, theta, theta_hw, eps), v)

@@ -529,3 +529,58 @@ def test_prefill_block_permutation_equivariance():
     o2 = oracle.prefill_attn(q[perm], k[perm], v[perm], idx, [0, T])
     np.testing.assert_allclose(o2[a:a + n], o1[perm[a:a + n]], rtol=0, atol=1e-12)
     np.testing.assert_allclose(o2[a + n:], o1[a + n:], rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------------------
+# Generation-branch q/k/v projection fused with the prologue: [A] §Mixture of Transformers
+# --------------------------------------------------------------------------------------
+
+def _proj_inputs(N=6, hidden=256, Hq=2, Hkv=1, seed=0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((N, hidden))
+    w = rng.standard_normal(((Hq + 2 * Hkv) * 128, hidden)) / np.sqrt(hidden)
+    nw = [rng.uniform(0.5, 1.5, 64) for _ in range(4)]
+    pos = np.stack([np.full(N, 7), np.arange(N) % 3, np.arange(N) // 3]).astype(np.int32)
+    return x, w, nw, pos
+
+
+def test_qkv_proj_selection_rows():
+    """With w_qkv rows selecting (permuted) columns of x, the projection is x[:, perm]: q and
+    k are the pinned prologue of those slices and v the slice itself -- catches a
+    transposed weight, a wrong q/k/v row order or a head reshaped the wrong way."""
+    N, hidden, Hq, Hkv = 5, 512, 2, 1
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((N, hidden))
+    perm = rng.permutation(hidden)
+    w = np.zeros(((Hq + 2 * Hkv) * 128, hidden))
+    w[np.arange(512), perm] = 1.0
+    _, _, nw, pos = _proj_inputs(N, hidden, Hq, Hkv)
+    q, k, v = oracle.qkv_proj_norm_rope(x, w, Hq, Hkv, *nw, pos)
+    xs = x[:, perm]
+    np.testing.assert_allclose(q, oracle.norm_rope(xs[:, :256].reshape(N, 2, 128), nw[0], nw[1], pos), atol=1e-13)
+    np.testing.assert_allclose(k, oracle.norm_rope(xs[:, 256:384].reshape(N, 1, 128), nw[2], nw[3], pos), atol=1e-13)
+    np.testing.assert_array_equal(v, xs[:, 384:].reshape(N, 1, 128))
+
+
+def test_qkv_proj_value_brute_force():
+    """v elements by explicit sums over the hidden dim (fsum), against the library matmul."""
+    x, w, nw, pos = _proj_inputs(seed=2)
+    _, _, v = oracle.qkv_proj_norm_rope(x, w, 2, 1, *nw, pos)
+    for t, f in [(0, 0), (3, 77), (5, 127)]:
+        ref = math.fsum(x[t, h] * w[(2 + 1) * 128 + f, h] for h in range(x.shape[1]))
+        assert v[t, 0, f] == pytest.approx(ref, abs=1e-12)
+
+
+def test_qkv_proj_scale_invariance_and_token_subset():
+    """RMSNorm makes q and k invariant to scaling x (up to eps) while v scales linearly;
+    evaluating a subset of tokens gives the same rows."""
+    x, w, nw, pos = _proj_inputs(N=9, seed=3)
+    q1, k1, v1 = oracle.qkv_proj_norm_rope(x, w, 2, 1, *nw, pos, eps=0.0)
+    q2, k2, v2 = oracle.qkv_proj_norm_rope(3.0 * x, w, 2, 1, *nw, pos, eps=0.0)
+    np.testing.assert_allclose(q2, q1, atol=1e-12)
+    np.testing.assert_allclose(k2, k1, atol=1e-12)
+    np.testing.assert_allclose(v2, 3.0 * v1, atol=1e-12)
+    rows = [8, 0, 4]
+    qs, ks, vs = oracle.qkv_proj_norm_rope(x, w, 2, 1, *nw, pos, eps=0.0, tokens=rows)
+    np.testing.assert_allclose(qs, q1[rows], atol=1e-13)
+    np.testing.assert_allclose(vs, v1[rows], atol=1e-13)
