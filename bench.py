@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--workload", default="large", choices=["large", "mid", "small", "editing"])
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--proj-steps", type=int, default=50,
+                    help="timed calls of the fused q/k/v projection + prologue on the workload's "
+                         "image tokens, beside a library GEMM plus the separate prologue (0 skips)")
     ap.add_argument("--prefill-steps", type=int, default=100,
                     help="timed calls of the block-causal prefill attention on the editing "
                          "workload's prefixes (0 skips it)")
@@ -297,6 +300,53 @@ def main():
         print(f"[bench] guided Euler step timed ({a.cfg_steps} calls per path)", file=sys.stderr,
               flush=True)
 
+    # the generation branch's q/k/v projection fused with the prologue, beside the unfused
+    # route (library bf16 GEMM, then the stand-alone norm + rotary pass)
+    proj = {}
+    if a.proj_steps > 0:
+        d = W.proj_inputs(w)
+        px = H.dev(W.bf16_round(d["x"]), "bf16")
+        pw = H.dev(W.bf16_round(d["w_qkv"]), "bf16")
+        hid = d["hidden"]
+        nq, nk = w.Hq * 128, w.Hkv * 128
+        pq = torch.empty((w.Tq, w.Hq, 128), dtype=torch.bfloat16, device=dev)
+        pk = torch.empty((w.Tq, w.Hkv, 128), dtype=torch.bfloat16, device=dev)
+        pv = torch.empty_like(pk)
+        nws = [shared[k_] for k_ in ("wq_t", "wq_hw", "wk_t", "wk_hw")]
+        pflops = 2.0 * w.Tq * hid * (nq + 2 * nk)
+
+        def fused():
+            neo.qkv_proj_norm_rope(px, pw, w.Hq, w.Hkv, *nws, shared["pos"], w.rope_theta,
+                                   w.rope_theta_hw, w.eps, q_out=pq, k_out=pk, v_out=pv)
+        y = torch.empty((w.Tq, nq + 2 * nk), dtype=torch.bfloat16, device=dev)
+
+        def unfused():
+            torch.matmul(px, pw.t(), out=y)
+            neo.qknorm_rope3(y[:, :nq].view(w.Tq, w.Hq, 128).contiguous(),
+                             y[:, nq:nq + nk].view(w.Tq, w.Hkv, 128).contiguous(), *nws,
+                             shared["pos"], w.rope_theta, w.rope_theta_hw, w.eps)
+
+        def timed(fn):
+            for _ in range(5):
+                fn()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(a.proj_steps)]
+            torch.cuda.synchronize()
+            for e0, e1 in evs:
+                e0.record()
+                fn()
+                e1.record()
+            torch.cuda.synchronize()
+            return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
+        us = timed(fused)
+        us_lib = timed(unfused)
+        proj = {"workload": f"{w.Tq} tokens x hidden {hid} -> {w.Hq}+{w.Hkv}+{w.Hkv} heads",
+                "gflop": pflops / 1e9, "us": us, "tflops": pflops / (us * 1e-6) / 1e12,
+                "frac": pflops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+                "unfused_library_gemm_plus_prologue_us": us_lib}
+        del px, pw, pq, pk, pv, y
+        print(f"[bench] fused projection timed ({a.proj_steps} calls)", file=sys.stderr, flush=True)
+
     # the understanding-pass (prefill) attention of the next row, on the editing workload's
     # four ragged prefixes (text, a 1024-token reference image, suffix)
     prefill = {}
@@ -375,6 +425,7 @@ def main():
                           "frac": (ntok / gpu_step_s) / (ntok / roof_step_s)},
         "cfg_euler": cfg,
         "prefill_attention": prefill,
+        "qkv_projection": proj,
     }
     print(json.dumps(result), flush=True)
 

@@ -159,6 +159,36 @@ neo_status neo_fm_euler_step(float *z, const float *x0_pred, int64_t n, float t,
                              float t_eps, void *hip_stream);
 
 /*
+ * neo_qkv_proj_norm_rope -- the generation branch's q/k/v projection of the
+ * noisy image tokens fused with the q/k prologue ([A] §Mixture of Transformers:
+ * the `_mot_gen` q/k/v projections and q/k norms; §Three rotary axes):
+ *     [q | k | v] = x w_qkv^T,  then q, k <- split-half RMSNorm + three-axis
+ *     rotary exactly as neo_qknorm_rope3 does,
+ * with the projection kept in fp32 on chip (no intermediate rounding) and one
+ * rounding to bf16 at the store.
+ *
+ *   x         [N, hidden] bf16 (the image tokens' hidden states), 16-byte aligned.
+ *   w_qkv     [(Hq + 2 Hkv) * 128, hidden] bf16: rows are the Hq query heads,
+ *             then the Hkv key heads, then the Hkv value heads (the three
+ *             projection matrices stacked; bf16 copies of the branch's weights).
+ *   hidden    a positive multiple of 64 (<= 2^20); head_dim must be 128.
+ *   q_norm_w, q_norm_hw_w, k_norm_w, k_norm_hw_w  [64] fp32 each.
+ *   pos_thw   [3, N] int32 temporal / height / width indices.
+ *   rope_theta, rope_theta_hw, eps   as for neo_qknorm_rope3.
+ *   q_out [N, Hq, 128], k_out [N, Hkv, 128], v_out [N, Hkv, 128] bf16; may not
+ *   overlap any input or each other.
+ *   dtype     NEO_BF16 only.
+ * Errors: NEO_ERR_SHAPE, NEO_ERR_VALUE, NEO_ERR_NULL, NEO_ERR_UNSUPPORTED, NEO_ERR_HIP.
+ */
+neo_status neo_qkv_proj_norm_rope(const void *x, const void *w_qkv, int64_t N, int32_t hidden,
+                                  int32_t Hq, int32_t Hkv, int32_t head_dim,
+                                  const float *q_norm_w, const float *q_norm_hw_w,
+                                  const float *k_norm_w, const float *k_norm_hw_w,
+                                  const int32_t *pos_thw, float rope_theta, float rope_theta_hw,
+                                  float eps, void *q_out, void *k_out, void *v_out,
+                                  neo_dtype dtype, void *hip_stream);
+
+/*
  * neo_prefill_attn_fwd -- understanding-pass (prefill) attention with the
  * block-causal mask ([A] §Block-causal attention; [B] §2.5, Fig. 6).  Within
  * each sample, query i attends key j when temporal_idx[j] == temporal_idx[i]

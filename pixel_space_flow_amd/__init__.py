@@ -13,7 +13,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["qknorm_rope3", "gen_attn_fwd", "prefill_attn_fwd", "fm_euler_step",
+__all__ = ["qknorm_rope3", "qkv_proj_norm_rope", "gen_attn_fwd", "prefill_attn_fwd",
+           "fm_euler_step",
            "fm_euler_step_cfg", "cfg_path",
            "NeoError", "lib", "LIB_PATH", "EXPORTED_SYMBOLS", "NEO_OK", "NEO_ERR_NULL", "NEO_ERR_SHAPE", "NEO_ERR_VALUE",
            "NEO_ERR_UNSUPPORTED", "NEO_ERR_HIP", "NEO_F32", "NEO_BF16"]
@@ -25,6 +26,7 @@ NEO_F32, NEO_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = ("neo_qknorm_rope3", "neo_gen_attn_fwd", "neo_fm_euler_step",
                     "neo_cfg_path", "neo_fm_euler_step_cfg", "neo_prefill_attn_fwd",
+                    "neo_qkv_proj_norm_rope",
                     "neo_status_string", "neo_last_error")
 
 _vp = ctypes.c_void_p
@@ -56,6 +58,10 @@ def lib() -> ctypes.CDLL:
                                        _i64, _i64, _i32, _i32, _f32, _vp, _vp, ctypes.c_int, _vp]
         L.neo_fm_euler_step.restype = ctypes.c_int
         L.neo_fm_euler_step.argtypes = [_vp, _vp, _i64, _f32, _f32, _f32, _vp]
+        L.neo_qkv_proj_norm_rope.restype = ctypes.c_int
+        L.neo_qkv_proj_norm_rope.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                             _vp, _vp, _f32, _f32, _f32, _vp, _vp, _vp,
+                                             ctypes.c_int, _vp]
         L.neo_prefill_attn_fwd.restype = ctypes.c_int
         L.neo_prefill_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64,
                                            _i32, _f32, _vp, _vp, ctypes.c_int, _vp]
@@ -176,6 +182,35 @@ def gen_attn_fwd(q, k_img, v_img, k_prefix, v_prefix, cu_seqlens_q, cu_seqlens_p
                                 _stream(q))
     _check("neo_gen_attn_fwd", st)
     return (out, lse) if return_lse else out
+
+
+def qkv_proj_norm_rope(x, w_qkv, Hq, Hkv, q_norm_w, q_norm_hw_w, k_norm_w, k_norm_hw_w, pos_thw,
+                       rope_theta=5.0e6, rope_theta_hw=1.0e4, eps=1e-6, q_out=None, k_out=None,
+                       v_out=None):
+    """The generation branch's q/k/v projection fused with the q/k prologue ([A] §Mixture of
+    Transformers, §Three rotary axes).  x [N, hidden] bf16; w_qkv [(Hq + 2 Hkv) * 128,
+    hidden] bf16 (q heads, then k heads, then v heads); norm weights [64] fp32; pos_thw
+    int32 [3, N].  Returns (q [N, Hq, 128], k [N, Hkv, 128], v [N, Hkv, 128]) bf16."""
+    torch = _torch()
+    _dev(x, "x", torch.bfloat16)
+    N, hidden = x.shape
+    _dev(w_qkv, "w_qkv", torch.bfloat16, ((Hq + 2 * Hkv) * 128, hidden))
+    for name, t in (("q_norm_w", q_norm_w), ("q_norm_hw_w", q_norm_hw_w),
+                    ("k_norm_w", k_norm_w), ("k_norm_hw_w", k_norm_hw_w)):
+        _dev(t, name, torch.float32, (64,))
+    _dev(pos_thw, "pos_thw", torch.int32, (3, N))
+    mk = lambda h: torch.empty((N, h, 128), dtype=torch.bfloat16, device=x.device)
+    q_out = mk(Hq) if q_out is None else _dev(q_out, "q_out", torch.bfloat16, (N, Hq, 128))
+    k_out = mk(Hkv) if k_out is None else _dev(k_out, "k_out", torch.bfloat16, (N, Hkv, 128))
+    v_out = mk(Hkv) if v_out is None else _dev(v_out, "v_out", torch.bfloat16, (N, Hkv, 128))
+    st = lib().neo_qkv_proj_norm_rope(x.data_ptr(), w_qkv.data_ptr(), N, hidden, Hq, Hkv, 128,
+                                      q_norm_w.data_ptr(), q_norm_hw_w.data_ptr(),
+                                      k_norm_w.data_ptr(), k_norm_hw_w.data_ptr(),
+                                      pos_thw.data_ptr(), float(rope_theta), float(rope_theta_hw),
+                                      float(eps), q_out.data_ptr(), k_out.data_ptr(),
+                                      v_out.data_ptr(), NEO_BF16, _stream(x))
+    _check("neo_qkv_proj_norm_rope", st)
+    return q_out, k_out, v_out
 
 
 def prefill_attn_fwd(q, k, v, temporal_idx, cu_seqlens, max_seqlen, softmax_scale=0.0, out=None,

@@ -202,6 +202,57 @@ neo_status neo_fm_euler_step(float* z, const float* x0_pred, int64_t n, float t,
                   "neo_fm_euler_step launch");
 }
 
+neo_status neo_qkv_proj_norm_rope(const void* x, const void* w_qkv, int64_t N, int32_t hidden,
+                                  int32_t Hq, int32_t Hkv, int32_t head_dim, const float* q_norm_w,
+                                  const float* q_norm_hw_w, const float* k_norm_w,
+                                  const float* k_norm_hw_w, const int32_t* pos_thw,
+                                  float rope_theta, float rope_theta_hw, float eps, void* q_out,
+                                  void* k_out, void* v_out, neo_dtype dtype, void* hip_stream) {
+  const char* fn = "neo_qkv_proj_norm_rope";
+  if (dtype != NEO_F32 && dtype != NEO_BF16)
+    return fail(NEO_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, (int)dtype);
+  if (dtype != NEO_BF16) return fail(NEO_ERR_UNSUPPORTED, "%s: bf16 only", fn);
+  if (head_dim != NEO_HEAD_DIM)
+    return fail(NEO_ERR_SHAPE, "%s: head_dim must be 128, got %d", fn, head_dim);
+  if (Hq < 1 || Hkv < 1 || Hq > 4096 || Hkv > 4096)
+    return fail(NEO_ERR_SHAPE, "%s: Hq=%d Hkv=%d out of range", fn, Hq, Hkv);
+  if (hidden < 64 || hidden % 64 != 0 || hidden > (1 << 20))
+    return fail(NEO_ERR_SHAPE, "%s: hidden=%d must be a positive multiple of 64 (<= 2^20)", fn, hidden);
+  if (N < 0 || N > (1 << 30)) return fail(NEO_ERR_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
+  if (!isfinite(rope_theta) || !isfinite(rope_theta_hw) || rope_theta <= 0.0f || rope_theta_hw <= 0.0f)
+    return fail(NEO_ERR_VALUE, "%s: rotary bases must be finite and > 0", fn);
+  if (!isfinite(eps) || eps < 0.0f) return fail(NEO_ERR_VALUE, "%s: eps must be finite and >= 0", fn);
+  {
+    const int64_t heads = (int64_t)Hq + 2 * Hkv;
+    const int64_t blocks = (heads * 128 + 255) / 256 * ((N + 127) / 128);
+    if (blocks >= ((int64_t)1 << 31)) return fail(NEO_ERR_SHAPE, "%s: problem too large for one launch", fn);
+  }
+  if (N == 0) return ok();
+  if (!x || !w_qkv || !q_norm_w || !q_norm_hw_w || !k_norm_w || !k_norm_hw_w || !pos_thw ||
+      !q_out || !k_out || !v_out)
+    return fail(NEO_ERR_NULL, "%s: a required pointer is NULL", fn);
+  const void* bufs[5] = {x, w_qkv, q_out, k_out, v_out};
+  for (const void* p : bufs)
+    if (!aligned16(p)) return fail(NEO_ERR_VALUE, "%s: x, w_qkv and outputs must be 16-byte aligned", fn);
+  const size_t xb = (size_t)N * hidden * 2, wb = ((size_t)Hq + 2 * Hkv) * 128 * hidden * 2;
+  const size_t qb = (size_t)N * Hq * 128 * 2, kb = (size_t)N * Hkv * 128 * 2;
+  const void* outs[3] = {q_out, k_out, v_out};
+  const size_t osz[3] = {qb, kb, kb};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(outs[i], osz[i], x, xb) || overlap(outs[i], osz[i], w_qkv, wb) ||
+        overlap(outs[i], osz[i], pos_thw, (size_t)N * 12))
+      return fail(NEO_ERR_VALUE, "%s: an output overlaps an input", fn);
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], osz[i], outs[j], osz[j]))
+        return fail(NEO_ERR_VALUE, "%s: outputs overlap", fn);
+  }
+  return from_hip(neo::launch_qkv_proj_bf16(x, w_qkv, N, hidden, Hq, Hkv, q_norm_w, q_norm_hw_w,
+                                            k_norm_w, k_norm_hw_w, pos_thw, rope_theta,
+                                            rope_theta_hw, eps, q_out, k_out, v_out,
+                                            static_cast<hipStream_t>(hip_stream)),
+                  "neo_qkv_proj_norm_rope launch");
+}
+
 neo_status neo_prefill_attn_fwd(const void* q, const void* k, const void* v,
                                 const int32_t* temporal_idx, const int32_t* cu_seqlens,
                                 int32_t B, int32_t Hq, int32_t Hkv, int32_t head_dim,

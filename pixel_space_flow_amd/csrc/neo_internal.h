@@ -35,6 +35,12 @@ hipError_t launch_gen_attn_f32(const float* q, const float* k_img, const float* 
                                float scale, float* out, float* lse, int64_t Tq, int64_t Tp,
                                hipStream_t stream);
 
+hipError_t launch_qkv_proj_bf16(const void* x, const void* w, int64_t N, int hidden, int Hq,
+                                int Hkv, const float* wq_t, const float* wq_hw, const float* wk_t,
+                                const float* wk_hw, const int32_t* pos, double theta,
+                                double theta_hw, float eps, void* q_out, void* k_out,
+                                void* v_out, hipStream_t stream);
+
 hipError_t launch_euler_step(float* z, const float* x0, int64_t n, float coef,
                              hipStream_t stream);
 

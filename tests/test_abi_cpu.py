@@ -239,3 +239,38 @@ def test_prefill_validation(L, kw, status):
 def test_prefill_empty_is_ok(L):
     assert _pre(L, mx=0, q=None) == P.NEO_OK
     assert _pre(L, T=0, mx=0) == P.NEO_OK
+
+
+def _proj(L, **kw):
+    a = dict(x=FAKE, w=FAKE + (1 << 30), N=4096, hidden=4096, Hq=32, Hkv=8, D=128, w0=W, w1=W,
+             w2=W, w3=W, pos=W + 4096, th=5e6, thw=1e4, eps=1e-6, q=FAKE + (2 << 30),
+             k=FAKE + (3 << 30), v=FAKE + (4 << 30), dtype=P.NEO_BF16)
+    a.update(kw)
+    return L.neo_qkv_proj_norm_rope(a["x"], a["w"], a["N"], a["hidden"], a["Hq"], a["Hkv"], a["D"],
+                                    a["w0"], a["w1"], a["w2"], a["w3"], a["pos"], a["th"],
+                                    a["thw"], a["eps"], a["q"], a["k"], a["v"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=P.NEO_F32), P.NEO_ERR_UNSUPPORTED),
+    (dict(D=64), P.NEO_ERR_SHAPE),
+    (dict(hidden=100), P.NEO_ERR_SHAPE),                         # not a multiple of 64
+    (dict(hidden=0), P.NEO_ERR_SHAPE),
+    (dict(Hkv=0), P.NEO_ERR_SHAPE),
+    (dict(N=-1), P.NEO_ERR_SHAPE),
+    (dict(th=-1.0), P.NEO_ERR_VALUE),
+    (dict(eps=math.inf), P.NEO_ERR_VALUE),
+    (dict(w=None), P.NEO_ERR_NULL),
+    (dict(pos=None), P.NEO_ERR_NULL),
+    (dict(v=None), P.NEO_ERR_NULL),
+    (dict(x=FAKE + 8), P.NEO_ERR_VALUE),                         # misaligned
+    (dict(k=FAKE + (2 << 30) + 4096), P.NEO_ERR_VALUE),          # k_out inside q_out
+    (dict(q=FAKE + 1024), P.NEO_ERR_VALUE),                      # q_out overlaps x
+])
+def test_proj_validation(L, kw, status):
+    assert _proj(L, **kw) == status
+    assert L.neo_last_error().decode().startswith("neo_qkv_proj_norm_rope")
+
+
+def test_proj_empty_is_ok(L):
+    assert _proj(L, N=0, x=None) == P.NEO_OK

@@ -501,3 +501,65 @@ def test_prefill_heads(neo, hq, hkv):
     d = W.prefill_layout([[("text", 40), ("image", 70), ("text", 9)], [("text", 33)]], hq, hkv,
                          seed=hq * 10 + hkv)
     _prefill_case(neo, d, f"Hq={hq} Hkv={hkv}")
+
+
+# --------------------------------------------------------------------------------------
+# Generation-branch q/k/v projection fused with the q/k prologue
+# --------------------------------------------------------------------------------------
+
+def _proj_case(neo, x, wq, Hq, Hkv, nw, pos, what, rows=None, theta=5.0e6, theta_hw=1.0e4,
+               eps=1e-6):
+    torch = _cuda()
+    xb, wb = W.bf16_round(x), W.bf16_round(wq)
+    _say(f"qkv proj {what}: N={x.shape[0]} hidden={x.shape[1]} Hq={Hq} Hkv={Hkv}")
+    q, k, v = neo.qkv_proj_norm_rope(H.dev(xb, "bf16"), H.dev(wb, "bf16"), Hq, Hkv,
+                                     *[H.dev_f32(a) for a in nw], H.dev_i32(pos), theta, theta_hw,
+                                     eps)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.qkv_proj_norm_rope(xb, wb, Hq, Hkv, *nw, pos, theta, theta_hw, eps,
+                                           tokens=rows)
+    sel = (lambda a: a[rows]) if rows is not None else (lambda a: a)
+    H.assert_close(sel(H.host(q)), rq, "bf16", f"qkv proj {what} q")
+    H.assert_close(sel(H.host(k)), rk, "bf16", f"qkv proj {what} k")
+    H.assert_close(sel(H.host(v)), rv, "bf16", f"qkv proj {what} v")
+
+
+@pytest.mark.parametrize("name", W.CONFIG_NAMES)
+def test_proj_configs(neo, name):
+    """Each workload's image tokens: hidden = Hq * 128; the full outputs for the smaller
+    workloads, sampled token rows (every 29th plus both ends) for the 4096-token ones."""
+    w = W.make(name, pixels=False)
+    d = W.proj_inputs(w)
+    rows = None
+    if w.Tq >= 4096:
+        rows = np.unique(np.concatenate([np.arange(0, w.Tq, 29), [w.Tq - 1]]))
+    _proj_case(neo, d["x"], d["w_qkv"], w.Hq, w.Hkv, (w.wq_t, w.wq_hw, w.wk_t, w.wk_hw),
+               w.pos_img, name, rows, w.rope_theta, w.rope_theta_hw, w.eps)
+
+
+@pytest.mark.parametrize("N,hidden,Hq,Hkv", [
+    (1, 64, 1, 1),          # one token, one stage of 64 hidden dims
+    (130, 192, 3, 1),       # ragged token tile, 5 heads (half-empty feature tile), 3 stages
+    (257, 256, 2, 2),       # 4 stages (loop break after one), two ragged token tiles
+    (96, 1024, 4, 1),       # 16 stages, tokens fewer than one tile
+])
+def test_proj_shapes(neo, N, hidden, Hq, Hkv):
+    _proj_random(neo, N, hidden, Hq, Hkv)
+
+
+def test_proj_half_tiles(neo):
+    """More 256x256 tiles than whole rounds of CUs: the surplus runs as 128-token halves,
+    one of which starts past the last token (4196 tokens, 48 heads); sampled rows incl. the
+    tail."""
+    N = 4196
+    rows = np.unique(np.concatenate([np.arange(0, N, 37), np.arange(N - 130, N)]))
+    _proj_random(neo, N, 4096, 32, 8, rows)
+
+
+def _proj_random(neo, N, hidden, Hq, Hkv, rows=None):
+    rng = np.random.default_rng(N + hidden)
+    x = rng.standard_normal((N, hidden)).astype(np.float32)
+    wq = (rng.standard_normal(((Hq + 2 * Hkv) * 128, hidden)) / np.sqrt(hidden)).astype(np.float32)
+    nw = tuple(rng.uniform(0.5, 1.5, 64).astype(np.float32) for _ in range(4))
+    pos = np.stack([np.full(N, 300 + N), rng.integers(0, 64, N), rng.integers(0, 64, N)]).astype(np.int32)
+    _proj_case(neo, x, wq, Hq, Hkv, nw, pos, f"N={N} hidden={hidden} Hq={Hq} Hkv={Hkv}", rows)

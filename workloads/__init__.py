@@ -295,3 +295,16 @@ def prefill_layout(segments, Hq: int, Hkv: int, seed: int = 0) -> dict:
     lens = np.diff(cu)
     return {"q": q, "k": k, "v": v, "idx": np.asarray(idx, dtype=np.int32),
             "cu": np.asarray(cu, dtype=np.int32), "max_len": int(lens.max()) if len(lens) else 0}
+
+
+def proj_inputs(w: Workload, seed: int = 0) -> dict:
+    """Inputs of the generation branch's q/k/v projection for workload w's image tokens:
+    hidden states x [Tq, Hq * 128] ~ N(0,1) and stacked weights w_qkv [(Hq + 2 Hkv) * 128,
+    Hq * 128] ~ N(0, 1/hidden) (q heads, then k, then v), fp32 draws from their own PCG64
+    stream; the workload's norm weights and image positions complete the inputs."""
+    rng = np.random.default_rng([seed, 0x7170])
+    hidden = w.Hq * 128
+    x = rng.standard_normal(size=(w.Tq, hidden), dtype=np.float32)
+    wq = rng.standard_normal(size=((w.Hq + 2 * w.Hkv) * 128, hidden), dtype=np.float32)
+    wq *= np.float32(1.0 / np.sqrt(hidden))
+    return {"x": x, "w_qkv": wq, "hidden": hidden}
