@@ -63,10 +63,10 @@ def parse():
 
 KERNELS = {"gen_attn_bf16_kernel": "gen_attn_bf16_kernel", "qknorm_rope3": "qknorm_rope3_kernel",
            "fm_euler_step": "euler_vec4_kernel", "prefill_attn_bf16_kernel": "prefill_attn_bf16_kernel",
-           "fm_euler_step_cfg": "euler_cfg_vec4_kernel"}
+           "fm_euler_step_cfg": "euler_cfg_vec4_kernel", "qkv_proj_bf16_kernel": "qkv_proj_bf16_kernel"}
 KERNEL_SOURCES = {"gen_attn_bf16_kernel": "gen_attn.hip", "qknorm_rope3": "qknorm_rope3.hip",
                   "fm_euler_step": "euler_step.hip", "prefill_attn_bf16_kernel": "gen_attn.hip",
-                  "fm_euler_step_cfg": "euler_step.hip"}
+                  "fm_euler_step_cfg": "euler_step.hip", "qkv_proj_bf16_kernel": "qkv_proj.hip"}
 
 
 def _counter_rows(d, counter):
@@ -115,6 +115,19 @@ def derive_traffic(a):
     with open(a.traffic_json, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
+
+
+def measured_bytes(a, key):
+    """HBM bytes per launch of kernel `key` from the stored counter runs, or None when they
+    were taken on another workload or before the kernel's source last changed."""
+    if not os.path.exists(a.traffic_json):
+        return None
+    with open(a.traffic_json) as f:
+        tj = json.load(f)
+    k = tj.get(key, {})
+    if tj.get("workload") != a.workload or k.get("source_sha256") != _kernel_source_hash(key):
+        return None
+    return k.get("bytes")
 
 
 def algorithmic(w):
@@ -250,14 +263,7 @@ def main():
 
     attn_s = float(att_ms.mean()) * 1e-3
     achieved = flops / attn_s / 1e12
-    traffic = None
-    if os.path.exists(a.traffic_json):
-        with open(a.traffic_json) as f:
-            tj = json.load(f)
-        att = tj.get("gen_attn_bf16_kernel", {})
-        if (tj.get("workload") == a.workload
-                and att.get("source_sha256") == _kernel_source_hash("gen_attn_bf16_kernel")):
-            traffic = att.get("bytes")
+    traffic = measured_bytes(a, "gen_attn_bf16_kernel")
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic}
     pro_gbs = pro_bytes / (float(pro_ms.mean()) * 1e-3) / 1e9
@@ -343,7 +349,8 @@ def main():
         proj = {"workload": f"{w.Tq} tokens x hidden {hid} -> {w.Hq}+{w.Hkv}+{w.Hkv} heads",
                 "gflop": pflops / 1e9, "us": us, "tflops": pflops / (us * 1e-6) / 1e12,
                 "frac": pflops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
-                "unfused_library_gemm_plus_prologue_us": us_lib}
+                "unfused_library_gemm_plus_prologue_us": us_lib,
+                "hbm_bytes_measured": measured_bytes(a, "qkv_proj_bf16_kernel")}
         del px, pw, pq, pk, pv, y
         print(f"[bench] fused projection timed ({a.proj_steps} calls)", file=sys.stderr, flush=True)
 

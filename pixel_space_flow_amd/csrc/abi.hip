@@ -47,6 +47,11 @@ bool rows_fit(int64_t t, int64_t h) {
   return t >= 0 && h >= 1 && t <= (int64_t)(INT64_MAX / 4) / h / neo::kHeadDim;
 }
 
+// workgroups x threads within the 32-bit work-item count of one dispatch
+bool grid_fits(int64_t blocks, int threads) {
+  return blocks >= 0 && blocks <= (int64_t)0xffffffffLL / threads;
+}
+
 }  // namespace
 
 extern "C" {
@@ -137,7 +142,7 @@ neo_status neo_gen_attn_fwd(const void* q, const void* k_img, const void* v_img,
     const int64_t G = Hq / Hkv;
     const int64_t per = dtype == NEO_BF16 ? ((int64_t)G * ((max_seqlen_q + 31) / 32) + 7) / 8
                                           : ((int64_t)max_seqlen_q * G + 127) / 128;
-    if (per * Hkv * B >= ((int64_t)1 << 31))
+    if (!grid_fits(per * Hkv * B, dtype == NEO_BF16 ? neo::kAttnBf16Threads : neo::kAttnF32Threads))
       return fail(NEO_ERR_SHAPE, "neo_gen_attn_fwd: problem too large for one launch");
   }
   if (max_seqlen_q == 0 || total_q == 0) return ok();
@@ -224,8 +229,10 @@ neo_status neo_qkv_proj_norm_rope(const void* x, const void* w_qkv, int64_t N, i
   if (!isfinite(eps) || eps < 0.0f) return fail(NEO_ERR_VALUE, "%s: eps must be finite and >= 0", fn);
   {
     const int64_t heads = (int64_t)Hq + 2 * Hkv;
-    const int64_t blocks = (heads * 128 + 255) / 256 * ((N + 127) / 128);
-    if (blocks >= ((int64_t)1 << 31)) return fail(NEO_ERR_SHAPE, "%s: problem too large for one launch", fn);
+    // 256 x 256 tiles; at most every tile runs as two halves
+    const int64_t blocks = 2 * ((heads * 128 + 255) / 256) * ((N + 255) / 256);
+    if (!grid_fits(blocks, neo::kProjThreads))
+      return fail(NEO_ERR_SHAPE, "%s: problem too large for one launch", fn);
   }
   if (N == 0) return ok();
   if (!x || !w_qkv || !q_norm_w || !q_norm_hw_w || !k_norm_w || !k_norm_hw_w || !pos_thw ||
@@ -279,7 +286,7 @@ neo_status neo_prefill_attn_fwd(const void* q, const void* k, const void* v,
   {
     const int64_t G = Hq / Hkv;
     const int64_t per = ((int64_t)G * ((max_seqlen + 31) / 32) + 7) / 8;
-    if (per * Hkv * B >= ((int64_t)1 << 31))
+    if (!grid_fits(per * Hkv * B, neo::kAttnBf16Threads))
       return fail(NEO_ERR_SHAPE, "%s: problem too large for one launch", fn);
   }
   if (max_seqlen == 0 || total == 0) return ok();

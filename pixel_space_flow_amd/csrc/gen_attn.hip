@@ -58,7 +58,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kThreads = 512;                // 8 waves, two per SIMD
+constexpr int kThreads = kAttnBf16Threads;   // 8 waves, two per SIMD
 constexpr int kWaves = kThreads / 64;
 constexpr int kBN = 64;                      // keys per LDS tile (one barrier per tile)
 constexpr int kRow = kHeadDim * 2;          // one K or V row in LDS (no padding)
@@ -527,7 +527,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_attn_bf16_kernel(
 // fp32 path
 // ---------------------------------------------------------------------------------------
 constexpr int kF32Keys = 32;
-constexpr int kF32Threads = 256;
+constexpr int kF32Threads = kAttnF32Threads;
 
 __global__ __launch_bounds__(kF32Threads) void gen_attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k_img, const float* __restrict__ v_img,

@@ -10,6 +10,12 @@ namespace neo {
 constexpr int kHeadDim = 128;
 constexpr int kHalfDim = 64;
 
+// threads per workgroup of the attention (bf16 / fp32) and projection launches; a launch's
+// work-items (workgroups x threads) must fit the dispatch's 32-bit grid size
+constexpr int kAttnBf16Threads = 512;
+constexpr int kAttnF32Threads = 256;
+constexpr int kProjThreads = 512;
+
 // ---- launchers (host side); each returns the hipError_t of its launch --------------
 
 hipError_t launch_qknorm_rope3(bool bf16, const void* q_in, const void* k_in, void* q_out,

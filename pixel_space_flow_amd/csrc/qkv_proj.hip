@@ -42,9 +42,10 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 512;           // 8 waves, two per SIMD
+constexpr int kThreads = kProjThreads;  // 8 waves, two per SIMD
 constexpr int kFT = 256;                // features per workgroup (two heads)
 constexpr int kTT = 256;                // tokens per workgroup
+constexpr int kGroup = 4;               // token tiles per group of the tile order
 constexpr int kKS = 64;                 // hidden dims per stage
 constexpr int kRowB = kKS * 2;          // one LDS tile row: 128 bytes = 8 chunks
 constexpr int kWTileB = kFT * kRowB;    // 32 KB
@@ -56,8 +57,15 @@ constexpr int kBufFlags = 0x00020000;   // raw buffer, 32-bit data format (gfx9 
 // pair's eight rows over the eight slots).
 __device__ __forceinline__ int pswz(int r) { return (r >> 1) & 7; }
 
+// The descriptor's fields are workgroup-uniform; passing them through readfirstlane keeps
+// them in scalar registers (the compiler otherwise may keep them in vector registers and
+// wrap every load in a loop over distinct descriptor values).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* up = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(up, (short)0, (int)__builtin_amdgcn_readfirstlane(nbytes),
                                            kBufFlags);
 }
 
@@ -290,7 +298,7 @@ __device__ __forceinline__ void proj_tile(
 // where the surplus is half the CU count, as at 4096 tokens and 48 heads).
 __global__ __launch_bounds__(kThreads, 1) void qkv_proj_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int N, int hidden, int Hq,
-    int Hkv, int n_ftiles, int n_full, int n_half, const float* __restrict__ wq_t,
+    int Hkv, int n_ftiles, int n_ttiles, int n_full, int n_half, const float* __restrict__ wq_t,
     const float* __restrict__ wq_hw, const float* __restrict__ wk_t,
     const float* __restrict__ wk_hw, const int32_t* __restrict__ pos, double r_t, double r_hw,
     float eps, uint16_t* __restrict__ q_out, uint16_t* __restrict__ k_out,
@@ -299,18 +307,26 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_bf16_kernel(
   // stage load cannot alias the fragment reads of the other stage
   __shared__ __attribute__((aligned(1024))) uint8_t lw0[kWTileB], lw1[kWTileB], lx0[kXTileB],
       lx1[kXTileB];
-  // within each kind the order is remapped so that an XCD's workgroups are neighbours
-  // (feature tiles fastest: they share one x tile)
+  // within each kind the order is remapped so that an XCD's workgroups take consecutive
+  // tile ids, and ids run over groups of kGroup token tiles (token tile fastest), so the
+  // 32 tiles an XCD holds at once form a 4 x 8 block that shares its x and W rows in L2
   const uint32_t b = blockIdx.x;
+  auto tile_of = [&](uint32_t id, int& ft, int& tt) __attribute__((always_inline)) {
+    const uint32_t per = (uint32_t)(kGroup * n_ftiles), g = id / per, r = id % per;
+    const int first = (int)g * kGroup;
+    const int gs = n_ttiles - first < kGroup ? n_ttiles - first : kGroup;
+    ft = (int)(r / (uint32_t)gs);
+    tt = first + (int)(r % (uint32_t)gs);
+  };
   if (b < (uint32_t)n_full) {
-    const uint32_t id = xcd_remap(b, (uint32_t)n_full);
-    const int ft = (int)(id % (uint32_t)n_ftiles), tt = (int)(id / (uint32_t)n_ftiles);
+    int ft, tt;
+    tile_of(xcd_remap(b, (uint32_t)n_full), ft, tt);
     proj_tile<2>(x, w, N, hidden, Hq, Hkv, ft * kFT, tt * kTT, wq_t, wq_hw, wk_t, wk_hw, pos, r_t,
                  r_hw, eps, q_out, k_out, v_out, lw0, lw1, lx0, lx1);
   } else {
     const uint32_t h = xcd_remap(b - (uint32_t)n_full, (uint32_t)n_half);
-    const uint32_t tile = (uint32_t)n_full + h / 2;
-    const int ft = (int)(tile % (uint32_t)n_ftiles), tt = (int)(tile / (uint32_t)n_ftiles);
+    int ft, tt;
+    tile_of((uint32_t)n_full + h / 2, ft, tt);
     proj_tile<1>(x, w, N, hidden, Hq, Hkv, ft * kFT, tt * kTT + 128 * (int)(h & 1), wq_t, wq_hw,
                  wk_t, wk_hw, pos, r_t, r_hw, eps, q_out, k_out, v_out, lw0, lw1, lx0, lx1);
   }
@@ -339,7 +355,7 @@ hipError_t launch_qkv_proj_bf16(const void* x, const void* w, int64_t N, int hid
   const double r_hw = pow(theta_hw, -2.0 / 32.0);
   hipLaunchKernelGGL(qkv_proj_bf16_kernel, dim3((unsigned)(n_full + n_half)), dim3(kThreads), 0,
                      stream, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), (int)N,
-                     hidden, Hq, Hkv, (int)n_ftiles, (int)n_full, (int)n_half, wq_t, wq_hw, wk_t,
+                     hidden, Hq, Hkv, (int)n_ftiles, (int)n_ttiles, (int)n_full, (int)n_half, wq_t, wq_hw, wk_t,
                      wk_hw, pos, r_t, r_hw, eps,
                      static_cast<uint16_t*>(q_out), static_cast<uint16_t*>(k_out),
                      static_cast<uint16_t*>(v_out));

@@ -109,6 +109,7 @@ def _attn(L, **kw):
     (dict(lse=FAKE + (5 << 30)), P.NEO_ERR_VALUE),             # lse overlaps out
     (dict(vi=FAKE + (2 << 30) + 4), P.NEO_ERR_VALUE),          # misaligned
     (dict(B=1 << 30, Hkv=8, mq=4096), P.NEO_ERR_SHAPE),        # grid beyond 2^31 workgroups
+    (dict(B=16384, Hkv=8, mq=4096), P.NEO_ERR_SHAPE),          # 2^23 workgroups of 512: > 2^32 - 1 work-items
     (dict(Tq=1 << 21, mq=1 << 21), P.NEO_ERR_SHAPE),            # one sample's K/V beyond 2 GiB
 ])
 def test_attn_validation(L, kw, status):
@@ -230,6 +231,7 @@ def _pre(L, **kw):
     (dict(out=FAKE + (2 << 30)), P.NEO_ERR_VALUE),              # out aliases v
     (dict(lse=FAKE + (3 << 30) + 4096), P.NEO_ERR_VALUE),       # lse inside out
     (dict(T=1 << 21, mx=1 << 21), P.NEO_ERR_SHAPE),             # one sample's K/V beyond 2 GiB
+    (dict(B=1 << 16), P.NEO_ERR_SHAPE),                          # grid beyond 2^32 work-items
 ])
 def test_prefill_validation(L, kw, status):
     assert _pre(L, **kw) == status
@@ -266,6 +268,7 @@ def _proj(L, **kw):
     (dict(x=FAKE + 8), P.NEO_ERR_VALUE),                         # misaligned
     (dict(k=FAKE + (2 << 30) + 4096), P.NEO_ERR_VALUE),          # k_out inside q_out
     (dict(q=FAKE + 1024), P.NEO_ERR_VALUE),                      # q_out overlaps x
+    (dict(N=1 << 26), P.NEO_ERR_SHAPE),                          # grid beyond 2^32 work-items
 ])
 def test_proj_validation(L, kw, status):
     assert _proj(L, **kw) == status
