@@ -2,9 +2,11 @@
 
 TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
 CPU-baseline leg use it; the HIP library never imports, links or calls it, and
-it never imports the library.  The arithmetic lives in ``neo_oracle.c`` (plain
-fp64 loops, cited there against the pages); this module only marshals numpy
-arrays through ctypes.
+it never imports the library.  The arithmetic of the attention block lives in
+``neo_oracle.c`` (plain fp64 loops, cited there against the pages) and this module
+marshals numpy arrays through ctypes to it; the q/k/v projection below is an fp64
+library matmul ahead of that code, and the generation branch's embedding front end
+is the numpy module ``front_end.py`` (fp64, each step from its definition).
 
 Pages cited:
   [A] "SenseNova-U1.5 (NEO-unify) architecture" (Mobius design note)

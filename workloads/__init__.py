@@ -308,3 +308,31 @@ def proj_inputs(w: Workload, seed: int = 0) -> dict:
     wq = rng.standard_normal(size=((w.Hq + 2 * w.Hkv) * 128, hidden), dtype=np.float32)
     wq *= np.float32(1.0 / np.sqrt(hidden))
     return {"x": x, "w_qkv": wq, "hidden": hidden}
+
+
+def embed_inputs(w: Workload, seed: int = 0, *, C1: int = 1024, D: int = 4096) -> dict:
+    """Inputs of the generation branch's embedding front end for workload w's pixel shape,
+    from their own PCG64 stream (seed key [seed, 0x656d]), all fp32:
+      z   [B, 3, H, W] = sigma_R * N(0,1) (the noisy image at the start of sampling);
+      w1  [C1, 3, 16, 16] ~ N(0, 1/768), b1 [C1] ~ N(0, 0.1^2)  (patch convolution);
+      w2  [D, C1, 2, 2] ~ N(0, 1/(4 C1)), b2 [D] ~ N(0, 0.1^2)  (2x2 merge convolution);
+      time and noise-scale embedders, each wa [D, 256] ~ N(0, 1/256), ba [D], wb [D, D]
+      ~ N(0, 1/D), bb [D] (biases ~ N(0, 0.1^2));
+      t (the second point of the time grid), noise_scale = sigma_R, noise_scale_max = 16.
+    The 1/fan-in variances keep every stage's outputs near unit size."""
+    rng = np.random.default_rng([seed, 0x656D])
+    Bn, C, H, Wd = w.pixel_shape
+    f32 = np.float32
+
+    def nrm(shape, var):
+        return (rng.standard_normal(size=shape, dtype=f32) * f32(np.sqrt(var))).astype(f32)
+
+    d = {"z": nrm((Bn, C, H, Wd), w.sigma_R ** 2)}
+    d["w1"], d["b1"] = nrm((C1, C, 16, 16), 1.0 / (C * 256)), nrm((C1,), 0.01)
+    d["w2"], d["b2"] = nrm((D, C1, 2, 2), 1.0 / (4 * C1)), nrm((D,), 0.01)
+    for e in ("t", "s"):
+        d[f"emb_{e}"] = (nrm((D, 256), 1.0 / 256), nrm((D,), 0.01), nrm((D, D), 1.0 / D),
+                         nrm((D,), 0.01))
+    d["t"] = float(w.t_grid[1]) if len(w.t_grid) > 1 else 0.5
+    d["noise_scale"], d["noise_scale_max"] = float(w.sigma_R), 16.0
+    return d
