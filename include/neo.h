@@ -268,6 +268,96 @@ const char *neo_status_string(neo_status s);
 /* Detail of the last non-OK return on the calling thread ("" if none). */
 const char *neo_last_error(void);
 
+/* ---- generation-branch embedding front end -------------------------------------
+ *
+ * Noisy pixels -> image-token embeddings, in four calls ([A] §Vision tower -- no
+ * transformer blocks; [B] §2.1, NEOVisionEmbeddings):
+ *   neo_gen_patchify      z -> 16x16 patch rows (bf16);
+ *   neo_gen_patch_embed   patch convolution + bias, GELU, interleaved two-axis rotary;
+ *   neo_gen_cond_hidden / neo_gen_cond_out   the time and noise-scale embedders ([A]
+ *                         §Timestep and noise-scale conditioning), summed;
+ *   neo_gen_merge_embed   2x2 stride-2 convolution + bias + the conditioning vector.
+ * Every intermediate is a caller buffer.  Convolution weights are bf16 (products in
+ * fp32), the embedder weights bf16, biases and vectors fp32.  Grids are row-major:
+ * patch (py, px) of image b is row b*P + py*(W/16) + px with P = (H/16)*(W/16); token
+ * (ty, tx) of image b is row b*(H/32)*(W/32) + ty*(W/32) + tx.  Every buffer is
+ * 16-byte aligned; outputs may not overlap inputs.
+ * Errors: NEO_ERR_SHAPE, NEO_ERR_VALUE, NEO_ERR_NULL, NEO_ERR_HIP.
+ */
+
+/*
+ * neo_gen_patchify -- the patch rearrangement of the noisy image ([A] §Flow
+ * matching without a VAE: patchify is a permutation), rounded to bf16 for the
+ * matrix cores.
+ *   z        [B, 3, H, W] fp32; H, W positive multiples of 16 (<= 32768).
+ *   patches  [B*P, 768] bf16: row = one 16x16 patch ordered (channel, ky, kx),
+ *            the order of a flattened [out, 3, 16, 16] convolution weight.
+ */
+neo_status neo_gen_patchify(const float *z, int32_t B, int32_t H, int32_t W, void *patches,
+                            void *hip_stream);
+
+/*
+ * neo_gen_patch_embed -- Conv2d(3, C1, kernel 16, stride 16) + bias, GELU
+ * (x * Phi(x), erf form), then the interleaved two-axis rotary of [A] §Vision
+ * tower: channels (2i, 2i+1) of the first C1/2 turn by the patch's column
+ * index px, those of the last C1/2 by its row index py, pair i of a half by
+ * position * rope_theta^(-2i/(C1/2)) (base 1e4 upstream).
+ *   patches  [B*P, 768] bf16 (neo_gen_patchify's output).
+ *   w1       [C1, 768] bf16: a [C1, 3, 16, 16] convolution weight, flattened.
+ *   b1       [C1] fp32.   C1: a positive multiple of 64 (<= 16384).
+ *   h_out    [B*P, C1] bf16, the rotated features.
+ */
+neo_status neo_gen_patch_embed(const void *patches, int32_t B, int32_t H, int32_t W,
+                               const void *w1, const float *b1, int32_t C1, float rope_theta,
+                               void *h_out, void *hip_stream);
+
+/*
+ * neo_gen_cond_hidden -- first layer of the time and noise-scale embedders:
+ *   hidden[0] = silu(wa_t e(t) + ba_t),
+ *   hidden[1] = silu(wa_s e(noise_scale / noise_scale_max) + ba_s),
+ * e(x) the 256-wide sinusoid basis [cos(x f_k), sin(x f_k)], f_k =
+ * 10000^(-k/128), k < 128, cosines first ([A] §Timestep and noise-scale
+ * conditioning).
+ *   wa_t, wa_s  [D, 256] bf16;  ba_t, ba_s [D] fp32;  D a positive multiple of 8.
+ *   hidden      [2, D] fp32.
+ */
+neo_status neo_gen_cond_hidden(float t, float noise_scale, float noise_scale_max, int32_t D,
+                               const void *wa_t, const float *ba_t, const void *wa_s,
+                               const float *ba_s, float *hidden, void *hip_stream);
+
+/*
+ * neo_gen_cond_out -- second layer of both embedders, summed: the vector added
+ * to every image token,
+ *   cond = wb_t hidden[0] + bb_t + wb_s hidden[1] + bb_s.
+ *   hidden [2, D] fp32 (neo_gen_cond_hidden's output); wb_t, wb_s [D, D] bf16;
+ *   bb_t, bb_s [D] fp32;  cond [D] fp32.
+ */
+neo_status neo_gen_cond_out(int32_t D, const float *hidden, const void *wb_t, const float *bb_t,
+                            const void *wb_s, const float *bb_s, float *cond, void *hip_stream);
+
+/*
+ * neo_gen_merge_embed -- Conv2d(C1, D, kernel 2, stride 2) + bias over the
+ * rotated patch features, plus the conditioning vector: the image-token
+ * embeddings ([A] §Vision tower's 2x2 merge into the backbone width, one token
+ * per 32x32 pixels; §Timestep and noise-scale conditioning).
+ *   h       [B*P, C1] bf16 (neo_gen_patch_embed's output); H, W positive
+ *           multiples of 32; B*P*C1*2 bytes below 2 GiB.
+ *   w2      [D, 2, 2, C1] bf16: a [D, C1, 2, 2] convolution weight with its
+ *           axes ordered (out, ky, kx, in), so that each window cell's C1
+ *           inputs are contiguous.
+ *   b2, cond [D] fp32;  D a positive multiple of 32 (<= 65536).
+ *   tokens  [B*(H/32)*(W/32), D] fp32.
+ */
+neo_status neo_gen_merge_embed(const void *h, int32_t B, int32_t H, int32_t W, int32_t C1,
+                               const void *w2, const float *b2, const float *cond, int32_t D,
+                               float *tokens, void *hip_stream);
+
+/*
+ * neo_shift_time -- the time-grid shift of [A] §Timestep schedule (host only):
+ *   sigma = 1 - t;  sigma <- shift sigma / (1 + (shift - 1) sigma);  returns 1 - sigma.
+ */
+double neo_shift_time(double t, double shift);
+
 #ifdef __cplusplus
 }
 #endif

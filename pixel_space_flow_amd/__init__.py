@@ -15,7 +15,8 @@ import os
 
 __all__ = ["qknorm_rope3", "qkv_proj_norm_rope", "gen_attn_fwd", "prefill_attn_fwd",
            "fm_euler_step",
-           "fm_euler_step_cfg", "cfg_path",
+           "fm_euler_step_cfg", "cfg_path", "gen_patchify", "gen_patch_embed",
+           "gen_cond_embed", "gen_merge_embed", "gen_embed", "shift_time",
            "NeoError", "lib", "LIB_PATH", "EXPORTED_SYMBOLS", "NEO_OK", "NEO_ERR_NULL", "NEO_ERR_SHAPE", "NEO_ERR_VALUE",
            "NEO_ERR_UNSUPPORTED", "NEO_ERR_HIP", "NEO_F32", "NEO_BF16"]
 
@@ -26,8 +27,9 @@ NEO_F32, NEO_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = ("neo_qknorm_rope3", "neo_gen_attn_fwd", "neo_fm_euler_step",
                     "neo_cfg_path", "neo_fm_euler_step_cfg", "neo_prefill_attn_fwd",
-                    "neo_qkv_proj_norm_rope",
-                    "neo_status_string", "neo_last_error")
+                    "neo_qkv_proj_norm_rope", "neo_gen_patchify", "neo_gen_patch_embed",
+                    "neo_gen_cond_hidden", "neo_gen_cond_out", "neo_gen_merge_embed",
+                    "neo_shift_time", "neo_status_string", "neo_last_error")
 
 _vp = ctypes.c_void_p
 _i32, _i64, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
@@ -69,6 +71,19 @@ def lib() -> ctypes.CDLL:
         L.neo_cfg_path.argtypes = [_f32] * 5
         L.neo_fm_euler_step_cfg.restype = ctypes.c_int
         L.neo_fm_euler_step_cfg.argtypes = [_vp, _vp, _vp, _vp, _i64] + [_f32] * 7 + [_vp]
+        L.neo_gen_patchify.restype = ctypes.c_int
+        L.neo_gen_patchify.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp]
+        L.neo_gen_patch_embed.restype = ctypes.c_int
+        L.neo_gen_patch_embed.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _f32, _vp, _vp]
+        L.neo_gen_cond_hidden.restype = ctypes.c_int
+        L.neo_gen_cond_hidden.argtypes = [_f32, _f32, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.neo_gen_cond_out.restype = ctypes.c_int
+        L.neo_gen_cond_out.argtypes = [_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.neo_gen_merge_embed.restype = ctypes.c_int
+        L.neo_gen_merge_embed.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp,
+                                          _vp]
+        L.neo_shift_time.restype = ctypes.c_double
+        L.neo_shift_time.argtypes = [ctypes.c_double, ctypes.c_double]
         L.neo_status_string.restype = ctypes.c_char_p
         L.neo_status_string.argtypes = [ctypes.c_int]
         L.neo_last_error.restype = ctypes.c_char_p
@@ -282,3 +297,102 @@ def fm_euler_step_cfg(z, x0_cond, x0_text_uncond=None, x0_uncond=None, *, t, t_n
                                      float(cfg_interval[1]), _stream(z))
     _check("neo_fm_euler_step_cfg", st)
     return z
+
+
+# ---- generation-branch embedding front end ([A] §Vision tower; §Timestep and noise-scale
+# conditioning; [B] §2.1) ------------------------------------------------------------------
+
+def gen_patchify(z, patches=None):
+    """z [B, 3, H, W] fp32 -> patch rows [B*P, 768] bf16 (channel, ky, kx order)."""
+    torch = _torch()
+    _dev(z, "z", torch.float32)
+    if z.dim() != 4 or z.shape[1] != 3:
+        raise ValueError(f"z must be [B, 3, H, W], got {tuple(z.shape)}")
+    B, _, H, W = z.shape
+    shape = (B * (H // 16) * (W // 16), 768)
+    patches = (torch.empty(shape, dtype=torch.bfloat16, device=z.device) if patches is None
+               else _dev(patches, "patches", torch.bfloat16, shape))
+    _check("neo_gen_patchify", lib().neo_gen_patchify(z.data_ptr(), B, H, W, patches.data_ptr(),
+                                                      _stream(z)))
+    return patches
+
+
+def gen_patch_embed(patches, B, H, W, w1, b1, rope_theta=1.0e4, h_out=None):
+    """Patch convolution + bias, GELU, interleaved two-axis rotary -> [B*P, C1] bf16.
+    w1: [C1, 768] bf16 (the [C1, 3, 16, 16] weight flattened), b1 [C1] fp32."""
+    torch = _torch()
+    P = (H // 16) * (W // 16)
+    _dev(patches, "patches", torch.bfloat16, (B * P, 768))
+    _dev(w1, "w1", torch.bfloat16)
+    C1 = w1.shape[0]
+    _dev(w1, "w1", torch.bfloat16, (C1, 768))
+    _dev(b1, "b1", torch.float32, (C1,))
+    h_out = (torch.empty((B * P, C1), dtype=torch.bfloat16, device=patches.device) if h_out is None
+             else _dev(h_out, "h_out", torch.bfloat16, (B * P, C1)))
+    st = lib().neo_gen_patch_embed(patches.data_ptr(), B, H, W, w1.data_ptr(), b1.data_ptr(), C1,
+                                   float(rope_theta), h_out.data_ptr(), _stream(patches))
+    _check("neo_gen_patch_embed", st)
+    return h_out
+
+
+def gen_cond_embed(t, noise_scale, noise_scale_max, emb_t, emb_s, hidden=None, cond=None):
+    """Time + noise-scale embedders summed -> cond [D] fp32.  emb_t, emb_s: (wa [D, 256] bf16,
+    ba [D] fp32, wb [D, D] bf16, bb [D] fp32).  Two calls; hidden [2, D] fp32 holds the
+    first layer's output.  Returns (cond, hidden)."""
+    torch = _torch()
+    D = emb_t[0].shape[0]
+    for tag, (wa, ba, wb, bb) in (("t", emb_t), ("s", emb_s)):
+        _dev(wa, f"wa_{tag}", torch.bfloat16, (D, 256))
+        _dev(ba, f"ba_{tag}", torch.float32, (D,))
+        _dev(wb, f"wb_{tag}", torch.bfloat16, (D, D))
+        _dev(bb, f"bb_{tag}", torch.float32, (D,))
+    dev = emb_t[0].device
+    hidden = (torch.empty((2, D), dtype=torch.float32, device=dev) if hidden is None
+              else _dev(hidden, "hidden", torch.float32, (2, D)))
+    cond = (torch.empty((D,), dtype=torch.float32, device=dev) if cond is None
+            else _dev(cond, "cond", torch.float32, (D,)))
+    s = _stream(emb_t[0])
+    st = lib().neo_gen_cond_hidden(float(t), float(noise_scale), float(noise_scale_max), D,
+                                   emb_t[0].data_ptr(), emb_t[1].data_ptr(), emb_s[0].data_ptr(),
+                                   emb_s[1].data_ptr(), hidden.data_ptr(), s)
+    _check("neo_gen_cond_hidden", st)
+    st = lib().neo_gen_cond_out(D, hidden.data_ptr(), emb_t[2].data_ptr(), emb_t[3].data_ptr(),
+                                emb_s[2].data_ptr(), emb_s[3].data_ptr(), cond.data_ptr(), s)
+    _check("neo_gen_cond_out", st)
+    return cond, hidden
+
+
+def gen_merge_embed(h, B, H, W, w2, b2, cond, tokens=None):
+    """2x2 stride-2 convolution + bias + cond -> tokens [B*(H/32)*(W/32), D] fp32.
+    h [B*P, C1] bf16; w2 [D, 2, 2, C1] bf16 (out, ky, kx, in); b2, cond [D] fp32."""
+    torch = _torch()
+    P = (H // 16) * (W // 16)
+    _dev(h, "h", torch.bfloat16)
+    C1 = h.shape[1]
+    _dev(h, "h", torch.bfloat16, (B * P, C1))
+    D = w2.shape[0]
+    _dev(w2, "w2", torch.bfloat16, (D, 2, 2, C1))
+    _dev(b2, "b2", torch.float32, (D,))
+    _dev(cond, "cond", torch.float32, (D,))
+    n = B * (H // 32) * (W // 32)
+    tokens = (torch.empty((n, D), dtype=torch.float32, device=h.device) if tokens is None
+              else _dev(tokens, "tokens", torch.float32, (n, D)))
+    st = lib().neo_gen_merge_embed(h.data_ptr(), B, H, W, C1, w2.data_ptr(), b2.data_ptr(),
+                                   cond.data_ptr(), D, tokens.data_ptr(), _stream(h))
+    _check("neo_gen_merge_embed", st)
+    return tokens
+
+
+def gen_embed(z, w1, b1, w2, b2, emb_t, emb_s, t, noise_scale, noise_scale_max,
+              rope_theta=1.0e4):
+    """The whole front end, z [B, 3, H, W] fp32 -> tokens [B*N, D] fp32 (five launches)."""
+    B, _, H, W = z.shape
+    patches = gen_patchify(z)
+    h = gen_patch_embed(patches, B, H, W, w1, b1, rope_theta)
+    cond, _ = gen_cond_embed(t, noise_scale, noise_scale_max, emb_t, emb_s)
+    return gen_merge_embed(h, B, H, W, w2, b2, cond)
+
+
+def shift_time(t, shift) -> float:
+    """The shifted time grid point of [A] §Timestep schedule (host only)."""
+    return float(lib().neo_shift_time(float(t), float(shift)))

@@ -7,6 +7,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <initializer_list>
+
 namespace {
 
 thread_local char g_err[512];
@@ -229,9 +231,7 @@ neo_status neo_qkv_proj_norm_rope(const void* x, const void* w_qkv, int64_t N, i
   if (!isfinite(eps) || eps < 0.0f) return fail(NEO_ERR_VALUE, "%s: eps must be finite and >= 0", fn);
   {
     const int64_t heads = (int64_t)Hq + 2 * Hkv;
-    // 256 x 256 tiles; at most every tile runs as two halves
-    const int64_t blocks = 2 * ((heads * 128 + 255) / 256) * ((N + 255) / 256);
-    if (!grid_fits(blocks, neo::kProjThreads))
+    if (!grid_fits(neo::gemm_max_blocks(heads * 128, N), neo::kGemmThreads))
       return fail(NEO_ERR_SHAPE, "%s: problem too large for one launch", fn);
   }
   if (N == 0) return ok();
@@ -371,6 +371,136 @@ neo_status neo_fm_euler_step_cfg(float* z, const float* x0_cond, const float* x0
   const float wf[3] = {(float)w[0], (float)w[1], (float)w[2]};
   return from_hip(neo::launch_euler_step_cfg(z, x, wf, nb, n, coef, static_cast<hipStream_t>(hip_stream)),
                   "neo_fm_euler_step_cfg launch");
+}
+
+// ---- generation-branch embedding front end ---------------------------------------------
+
+namespace {
+
+// H and W positive multiples of m and small enough that every count below fits
+bool image_ok(int32_t B, int32_t H, int32_t W, int m) {
+  return B >= 0 && B <= (1 << 16) && H >= m && W >= m && H % m == 0 && W % m == 0 &&
+         H <= (1 << 15) && W <= (1 << 15);
+}
+
+bool all16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!aligned16(p)) return false;
+  return true;
+}
+
+}  // namespace
+
+neo_status neo_gen_patchify(const float* z, int32_t B, int32_t H, int32_t W, void* patches,
+                            void* hip_stream) {
+  const char* fn = "neo_gen_patchify";
+  if (!image_ok(B, H, W, 16))
+    return fail(NEO_ERR_SHAPE, "%s: B=%d H=%d W=%d (H, W positive multiples of 16, <= 32768)", fn, B, H, W);
+  if (B == 0) return ok();
+  if (!z || !patches) return fail(NEO_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (!all16({z, patches})) return fail(NEO_ERR_VALUE, "%s: buffers must be 16-byte aligned", fn);
+  const size_t zb = (size_t)B * 3 * H * W * 4, pb = (size_t)B * 3 * H * W * 2;
+  if (overlap(z, zb, patches, pb)) return fail(NEO_ERR_VALUE, "%s: patches overlap z", fn);
+  return from_hip(neo::launch_gen_patchify(z, B, H, W, patches, static_cast<hipStream_t>(hip_stream)),
+                  "neo_gen_patchify launch");
+}
+
+neo_status neo_gen_patch_embed(const void* patches, int32_t B, int32_t H, int32_t W,
+                               const void* w1, const float* b1, int32_t C1, float rope_theta,
+                               void* h_out, void* hip_stream) {
+  const char* fn = "neo_gen_patch_embed";
+  if (!image_ok(B, H, W, 16))
+    return fail(NEO_ERR_SHAPE, "%s: B=%d H=%d W=%d (H, W positive multiples of 16, <= 32768)", fn, B, H, W);
+  if (C1 < 64 || C1 % 64 != 0 || C1 > 16384)
+    return fail(NEO_ERR_SHAPE, "%s: C1=%d must be a positive multiple of 64 (<= 16384)", fn, C1);
+  if (!finite(rope_theta) || rope_theta <= 1.0f)
+    return fail(NEO_ERR_VALUE, "%s: rope_theta must be finite and > 1", fn);
+  const int64_t M = (int64_t)B * (H / 16) * (W / 16);
+  if (!grid_fits(neo::gemm_max_blocks(C1, M), neo::kGemmThreads))
+    return fail(NEO_ERR_SHAPE, "%s: problem too large for one launch", fn);
+  if (M == 0) return ok();
+  if (!patches || !w1 || !b1 || !h_out) return fail(NEO_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (!all16({patches, w1, b1, h_out})) return fail(NEO_ERR_VALUE, "%s: buffers must be 16-byte aligned", fn);
+  const size_t hb = (size_t)M * C1 * 2;
+  if (overlap(h_out, hb, patches, (size_t)M * 768 * 2) || overlap(h_out, hb, w1, (size_t)C1 * 768 * 2) ||
+      overlap(h_out, hb, b1, (size_t)C1 * 4))
+    return fail(NEO_ERR_VALUE, "%s: h_out overlaps an input", fn);
+  return from_hip(neo::launch_gen_patch_embed(patches, B, H, W, w1, b1, C1, (double)rope_theta, h_out,
+                                              static_cast<hipStream_t>(hip_stream)),
+                  "neo_gen_patch_embed launch");
+}
+
+neo_status neo_gen_cond_hidden(float t, float noise_scale, float noise_scale_max, int32_t D,
+                               const void* wa_t, const float* ba_t, const void* wa_s,
+                               const float* ba_s, float* hidden, void* hip_stream) {
+  const char* fn = "neo_gen_cond_hidden";
+  if (D < 8 || D % 8 != 0 || D > (1 << 20))
+    return fail(NEO_ERR_SHAPE, "%s: D=%d must be a positive multiple of 8 (<= 2^20)", fn, D);
+  if (!finite(t) || !finite(noise_scale) || !finite(noise_scale_max) || noise_scale_max <= 0.0f)
+    return fail(NEO_ERR_VALUE, "%s: t and the noise scale must be finite, its maximum > 0", fn);
+  if (!wa_t || !ba_t || !wa_s || !ba_s || !hidden)
+    return fail(NEO_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (!all16({wa_t, ba_t, wa_s, ba_s, hidden}))
+    return fail(NEO_ERR_VALUE, "%s: buffers must be 16-byte aligned", fn);
+  const size_t hb = (size_t)2 * D * 4, wab = (size_t)D * 256 * 2, bab = (size_t)D * 4;
+  if (overlap(hidden, hb, wa_t, wab) || overlap(hidden, hb, wa_s, wab) ||
+      overlap(hidden, hb, ba_t, bab) || overlap(hidden, hb, ba_s, bab))
+    return fail(NEO_ERR_VALUE, "%s: hidden overlaps an input", fn);
+  const float arg_s = (float)((double)noise_scale / (double)noise_scale_max);
+  return from_hip(neo::launch_gen_cond_hidden(t, arg_s, D, wa_t, ba_t, wa_s, ba_s, hidden,
+                                              static_cast<hipStream_t>(hip_stream)),
+                  "neo_gen_cond_hidden launch");
+}
+
+neo_status neo_gen_cond_out(int32_t D, const float* hidden, const void* wb_t, const float* bb_t,
+                            const void* wb_s, const float* bb_s, float* cond, void* hip_stream) {
+  const char* fn = "neo_gen_cond_out";
+  if (D < 8 || D % 8 != 0 || D > (1 << 20))
+    return fail(NEO_ERR_SHAPE, "%s: D=%d must be a positive multiple of 8 (<= 2^20)", fn, D);
+  if (!hidden || !wb_t || !bb_t || !wb_s || !bb_s || !cond)
+    return fail(NEO_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (!all16({hidden, wb_t, bb_t, wb_s, bb_s, cond}))
+    return fail(NEO_ERR_VALUE, "%s: buffers must be 16-byte aligned", fn);
+  const size_t cb = (size_t)D * 4, wbb = (size_t)D * D * 2;
+  if (overlap(cond, cb, hidden, 2 * cb) || overlap(cond, cb, wb_t, wbb) || overlap(cond, cb, wb_s, wbb) ||
+      overlap(cond, cb, bb_t, cb) || overlap(cond, cb, bb_s, cb))
+    return fail(NEO_ERR_VALUE, "%s: cond overlaps an input", fn);
+  return from_hip(neo::launch_gen_cond_out(D, hidden, wb_t, bb_t, wb_s, bb_s, cond,
+                                           static_cast<hipStream_t>(hip_stream)),
+                  "neo_gen_cond_out launch");
+}
+
+neo_status neo_gen_merge_embed(const void* h, int32_t B, int32_t H, int32_t W, int32_t C1,
+                               const void* w2, const float* b2, const float* cond, int32_t D,
+                               float* tokens, void* hip_stream) {
+  const char* fn = "neo_gen_merge_embed";
+  if (!image_ok(B, H, W, 32))
+    return fail(NEO_ERR_SHAPE, "%s: B=%d H=%d W=%d (H, W positive multiples of 32, <= 32768)", fn, B, H, W);
+  if (C1 < 64 || C1 % 64 != 0 || C1 > 16384)
+    return fail(NEO_ERR_SHAPE, "%s: C1=%d must be a positive multiple of 64 (<= 16384)", fn, C1);
+  if (D < 32 || D % 32 != 0 || D > (1 << 16))
+    return fail(NEO_ERR_SHAPE, "%s: D=%d must be a positive multiple of 32 (<= 65536)", fn, D);
+  const int64_t P = (int64_t)(H / 16) * (W / 16), Ntot = (int64_t)B * (H / 32) * (W / 32);
+  // the gathered input rows are addressed with 32-bit byte offsets
+  if ((int64_t)B * P * C1 * 2 >= ((int64_t)1 << 31))
+    return fail(NEO_ERR_SHAPE, "%s: the patch features exceed 2 GiB", fn);
+  if (!grid_fits(neo::gemm_max_blocks(D, Ntot), neo::kGemmThreads))
+    return fail(NEO_ERR_SHAPE, "%s: problem too large for one launch", fn);
+  if (Ntot == 0) return ok();
+  if (!h || !w2 || !b2 || !cond || !tokens) return fail(NEO_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (!all16({h, w2, b2, cond, tokens})) return fail(NEO_ERR_VALUE, "%s: buffers must be 16-byte aligned", fn);
+  const size_t tb = (size_t)Ntot * D * 4;
+  if (overlap(tokens, tb, h, (size_t)B * P * C1 * 2) || overlap(tokens, tb, w2, (size_t)D * 4 * C1 * 2) ||
+      overlap(tokens, tb, b2, (size_t)D * 4) || overlap(tokens, tb, cond, (size_t)D * 4))
+    return fail(NEO_ERR_VALUE, "%s: tokens overlap an input", fn);
+  return from_hip(neo::launch_gen_merge_embed(h, B, H, W, C1, w2, b2, cond, D, tokens,
+                                              static_cast<hipStream_t>(hip_stream)),
+                  "neo_gen_merge_embed launch");
+}
+
+double neo_shift_time(double t, double shift) {
+  const double sigma = 1.0 - t;
+  return 1.0 - shift * sigma / (1.0 + (shift - 1.0) * sigma);
 }
 
 }  // extern "C"

@@ -1,0 +1,373 @@
+// The generation branch's embedding front end: noisy pixels -> image-token embeddings.
+//
+// "SenseNova-U1.5 (NEO-unify) architecture", §Vision tower -- no transformer blocks: a
+// 16x16 stride-16 patch convolution, GELU, an interleaved two-axis rotary (base 1e4; the
+// first half of the channels turns with the column position, the second half with the row
+// position), and a 2x2 stride-2 convolution into the backbone width -- one token per 32x32
+// pixels.  §Timestep and noise-scale conditioning: two embedders over a 256-wide [cos, sin]
+// sinusoid basis (the noise scale normalised by its maximum) whose outputs are summed and
+// added to every image token.  "SenseNova-U1 ... NEO-unify Architecture" §2.1 prints the
+// two convolutions of NEOVisionEmbeddings.
+//
+// Kernels:
+//   patchify_bf16_kernel   pixels fp32 [B, 3, H, W] -> patch rows bf16 [B P, 768], ordered
+//                          (channel, ky, kx) like a flattened convolution weight (streaming);
+//   patch_gemm_kernel      rows x w1^T on the shared MFMA tile core, epilogue bias + GELU +
+//                          rotary, bf16 features [B P, C1];
+//   cond_hidden_kernel     first embedder layer: silu(wa e + ba) for both embedders (one
+//                          wave per output row; reads wa once);
+//   cond_out_kernel        second layer: wb_t h_t + bb_t + wb_s h_s + bb_s (one wave per
+//                          row; streams wb once);
+//   merge_gemm_kernel      the 2x2 convolution as a matrix product whose input rows are
+//                          gathered from the patch features (each 64-wide K stage lies in
+//                          one window cell, so a row's offset is its top-left patch plus a
+//                          per-stage cell offset), epilogue + b2 + cond, fp32 tokens.
+#include "gemm_tile.h"
+
+#include <math.h>
+
+namespace neo {
+namespace {
+
+using gemm::f32x16;
+using gemm::kThreads;
+
+constexpr int kPatch = 16;
+constexpr int kPatchK = 3 * kPatch * kPatch;  // 768
+constexpr int kStreamThreads = 256;
+constexpr int kSinDim = 256;
+
+int64_t stream_grid(int64_t items) {
+  int64_t blocks = (items + kStreamThreads - 1) / kStreamThreads;
+  const int64_t cap = 256 * 32;
+  return blocks < 1 ? 1 : (blocks > cap ? cap : blocks);
+}
+
+// ---- patchify --------------------------------------------------------------------------
+// One item = 16 pixels of one (image, channel, pixel row, patch column): 64 contiguous
+// bytes read (consecutive items are consecutive in memory) and 32 bytes written into the
+// patch's row at (channel, ky).
+__global__ __launch_bounds__(kStreamThreads) void patchify_bf16_kernel(
+    const float* __restrict__ z, int64_t items, int H, int gw, int64_t P,
+    uint16_t* __restrict__ patches) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < items; i += stride) {
+    const int px = (int)(i % gw);
+    int64_t rest = i / gw;
+    const int y = (int)(rest % H);
+    rest /= H;
+    const int c = (int)(rest % 3);
+    const int64_t b = rest / 3;
+    const float4* src = reinterpret_cast<const float4*>(z + i * kPatch);
+    const float4 a0 = src[0], a1 = src[1], a2 = src[2], a3 = src[3];
+    const int py = y >> 4, ky = y & 15;
+    uint16_t* dst = patches + (b * P + (int64_t)py * gw + px) * kPatchK + c * 256 + ky * 16;
+    uint4 lo, hi;
+    lo.x = pack_bf16x2(a0.x, a0.y); lo.y = pack_bf16x2(a0.z, a0.w);
+    lo.z = pack_bf16x2(a1.x, a1.y); lo.w = pack_bf16x2(a1.z, a1.w);
+    hi.x = pack_bf16x2(a2.x, a2.y); hi.y = pack_bf16x2(a2.z, a2.w);
+    hi.z = pack_bf16x2(a3.x, a3.y); hi.w = pack_bf16x2(a3.z, a3.w);
+    reinterpret_cast<uint4*>(dst)[0] = lo;
+    reinterpret_cast<uint4*>(dst)[1] = hi;
+  }
+}
+
+// ---- patch convolution + GELU + rotary --------------------------------------------------
+template <int TW>
+__device__ __forceinline__ void patch_tile(const uint16_t* __restrict__ patches,
+                                           const uint16_t* __restrict__ w1,
+                                           const float* __restrict__ b1, int64_t M, int C1,
+                                           int gw, int P, float l2f, int f0, int t0,
+                                           uint16_t* __restrict__ hout, uint8_t* lw0,
+                                           uint8_t* lw1, uint8_t* lx0, uint8_t* lx1) {
+  constexpr int kTTile = 128 * TW;
+  const int lane = threadIdx.x & 63, hl = lane >> 5, col = lane & 31;
+  const int wave = threadIdx.x >> 6, hh = wave >> 2, tg = wave & 3;
+  constexpr uint32_t kRowBytes = kPatchK * 2;
+  const int wrows = C1 - f0 < gemm::kFT ? C1 - f0 : gemm::kFT;
+  const int64_t xleft = M - t0 < 0 ? 0 : M - t0;
+  const int xrows = xleft < kTTile ? (int)xleft : kTTile;
+  const __amdgpu_buffer_rsrc_t rw = gemm::make_rsrc(w1 + (int64_t)f0 * kPatchK, (uint32_t)wrows * kRowBytes);
+  const __amdgpu_buffer_rsrc_t rx =
+      gemm::make_rsrc(patches + (int64_t)t0 * kPatchK, (uint32_t)xrows * kRowBytes);
+  f32x16 acc[TW][4];
+  gemm::mainloop<TW>(
+      acc, rw, kRowBytes, rx,
+      [&](int r) __attribute__((always_inline)) { return (uint32_t)r * kRowBytes; },
+      [&](int s) __attribute__((always_inline)) { return (uint32_t)(s * gemm::kRowB); },
+      kPatchK / gemm::kKS, lw0, lw1, lx0, lx1);
+
+  const int half_c = C1 >> 1;
+#pragma unroll
+  for (int ti = 0; ti < TW; ++ti) {
+    const int64_t m = (int64_t)t0 + tg * 32 * TW + ti * 32 + col;  // patch row
+    if (m >= M) continue;
+    const int mi = (int)(m % P);
+    const float px = (float)(mi % gw), py = (float)(mi / gw);
+#pragma unroll
+    for (int fi = 0; fi < 4; ++fi) {
+      const int fb = f0 + 128 * hh + 32 * fi;  // first feature of this accumulator
+      if (fb >= C1) continue;
+      uint16_t* orow = hout + m * C1 + fb;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int f = fb + rg * 8 + 4 * hl + e;
+          const float x = acc[ti][fi][rg * 4 + e] + b1[f];
+          v[e] = 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+        }
+        // pairs (f, f + 1), f even: elements e = 0, 1 and 2, 3
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const int f = fb + rg * 8 + 4 * hl + e;
+          const bool second = f >= half_c;
+          const int i = ((second ? f - half_c : f) >> 1);
+          const float phi = (second ? py : px) * exp2f(-(float)i * l2f);
+          float sn, cs;
+          sincosf(phi, &sn, &cs);
+          const float a = v[e], b = v[e + 1];
+          v[e] = a * cs - b * sn;
+          v[e + 1] = a * sn + b * cs;
+        }
+        *reinterpret_cast<uint2*>(orow + rg * 8 + 4 * hl) =
+            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void patch_gemm_kernel(
+    const uint16_t* __restrict__ patches, const uint16_t* __restrict__ w1,
+    const float* __restrict__ b1, int64_t M, int C1, int gw, int P, float l2f, gemm::Plan plan,
+    uint16_t* __restrict__ hout) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lw0[gemm::kWTileB], lw1[gemm::kWTileB],
+      lx0[gemm::kXTileB], lx1[gemm::kXTileB];
+  const gemm::Tile tl = gemm::tile_of(blockIdx.x, plan);
+  if (tl.full)
+    patch_tile<2>(patches, w1, b1, M, C1, gw, P, l2f, tl.f0, tl.t0, hout, lw0, lw1, lx0, lx1);
+  else
+    patch_tile<1>(patches, w1, b1, M, C1, gw, P, l2f, tl.f0, tl.t0, hout, lw0, lw1, lx0, lx1);
+}
+
+// ---- time and noise-scale embedders ----------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Row j of embedder e (0: time, 1: noise scale): hidden[e][j] = silu(wa_e[j] . basis_e + ba_e[j])
+// with basis_e the [cos, sin] sinusoid of arg[e]; lane l takes basis entries 4l .. 4l+3.
+__global__ __launch_bounds__(kStreamThreads) void cond_hidden_kernel(
+    float arg_t, float arg_s, int D, const uint16_t* __restrict__ wa_t,
+    const float* __restrict__ ba_t, const uint16_t* __restrict__ wa_s,
+    const float* __restrict__ ba_s, float* __restrict__ hidden) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kStreamThreads / 64) + (threadIdx.x >> 6);
+  if (row >= 2 * (int64_t)D) return;
+  const int e = row >= D ? 1 : 0;
+  const int j = (int)(row - (int64_t)e * D);
+  const float arg = e ? arg_s : arg_t;
+  const uint16_t* wa = (e ? wa_s : wa_t) + (int64_t)j * kSinDim;
+  const uint2 wv = *reinterpret_cast<const uint2*>(wa + 4 * lane);
+  const float w4[4] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y)};
+  // frequencies exp(-ln(10000) k / 128) = 2^(-k log2(10000) / 128)
+  constexpr float kL2 = 13.287712379549449f / 128.0f;
+  float acc = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = 4 * lane + q;
+    const int k = i & 127;
+    float sn, cs;
+    sincosf(arg * exp2f(-(float)k * kL2), &sn, &cs);
+    acc = fmaf(w4[q], i < 128 ? cs : sn, acc);
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) {
+    const float x = acc + (e ? ba_s : ba_t)[j];
+    hidden[row] = x / (1.0f + expf(-x));
+  }
+}
+
+// cond[j] = wb_t[j] . hidden[0] + bb_t[j] + wb_s[j] . hidden[1] + bb_s[j]: one wave per row,
+// lane l reading 16-byte chunks l, l + 64, ... of both weight rows.
+__global__ __launch_bounds__(kStreamThreads) void cond_out_kernel(
+    int D, const float* __restrict__ hidden, const uint16_t* __restrict__ wb_t,
+    const float* __restrict__ bb_t, const uint16_t* __restrict__ wb_s,
+    const float* __restrict__ bb_s, float* __restrict__ cond) {
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x * (kStreamThreads / 64) + (threadIdx.x >> 6);
+  if (j >= D) return;
+  const int chunks = D >> 3;
+  float acc = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const uint4* wr = reinterpret_cast<const uint4*>((e ? wb_s : wb_t) + (int64_t)j * D);
+    const float4* hv = reinterpret_cast<const float4*>(hidden + (int64_t)e * D);
+    for (int c = lane; c < chunks; c += 64) {
+      const uint4 w8 = wr[c];
+      const float4 h0 = hv[2 * c], h1 = hv[2 * c + 1];
+      acc = fmaf(bf16_lo(w8.x), h0.x, acc);
+      acc = fmaf(bf16_hi(w8.x), h0.y, acc);
+      acc = fmaf(bf16_lo(w8.y), h0.z, acc);
+      acc = fmaf(bf16_hi(w8.y), h0.w, acc);
+      acc = fmaf(bf16_lo(w8.z), h1.x, acc);
+      acc = fmaf(bf16_hi(w8.z), h1.y, acc);
+      acc = fmaf(bf16_lo(w8.w), h1.z, acc);
+      acc = fmaf(bf16_hi(w8.w), h1.w, acc);
+    }
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) cond[j] = acc + bb_t[j] + bb_s[j];
+}
+
+// ---- 2x2 merge convolution + bias + conditioning ----------------------------------------
+template <int TW>
+__device__ __forceinline__ void merge_tile(const uint16_t* __restrict__ h,
+                                           const uint16_t* __restrict__ w2,
+                                           const float* __restrict__ b2,
+                                           const float* __restrict__ cond, int64_t Ntot,
+                                           int Nimg, int tw, int gw, int64_t P, int C1, int D,
+                                           uint32_t h_bytes, int S, int f0, int t0,
+                                           float* __restrict__ tokens, uint8_t* lw0,
+                                           uint8_t* lw1, uint8_t* lx0, uint8_t* lx1) {
+  const int lane = threadIdx.x & 63, hl = lane >> 5, col = lane & 31;
+  const int wave = threadIdx.x >> 6, hh = wave >> 2, tg = wave & 3;
+  const uint32_t w_row_bytes = (uint32_t)C1 * 8;   // K = 4 C1 bf16
+  const uint32_t h_row_bytes = (uint32_t)C1 * 2;
+  const int wrows = D - f0 < gemm::kFT ? D - f0 : gemm::kFT;
+  const __amdgpu_buffer_rsrc_t rw = gemm::make_rsrc(w2 + (int64_t)f0 * 4 * C1, (uint32_t)wrows * w_row_bytes);
+  const __amdgpu_buffer_rsrc_t rx = gemm::make_rsrc(h, h_bytes);
+  const int cpr = C1 / gemm::kKS;  // K stages per window cell
+  f32x16 acc[TW][4];
+  gemm::mainloop<TW, true>(
+      acc, rw, w_row_bytes, rx,
+      [&](int r) __attribute__((always_inline)) {
+        // the token's top-left patch row (cell dy = dx = 0); every count here is below
+        // 2^31 (the features are under 2 GiB), so 32-bit arithmetic is exact
+        const uint32_t n = (uint32_t)t0 + (uint32_t)r;
+        if (n >= (uint32_t)Ntot) return gemm::kAbsentRow;
+        const uint32_t b = n / (uint32_t)Nimg, m = n - b * (uint32_t)Nimg;
+        const uint32_t ty = m / (uint32_t)tw, tx = m - ty * (uint32_t)tw;
+        return (b * (uint32_t)P + 2 * ty * (uint32_t)gw + 2 * tx) * h_row_bytes;
+      },
+      [&](int s) __attribute__((always_inline)) {
+        // window cell q = s / cpr (s < 4 cpr), (dy, dx) = (q / 2, q % 2)
+        const int q = (s >= cpr) + (s >= 2 * cpr) + (s >= 3 * cpr), cs = s - q * cpr;
+        return (uint32_t)(((q >> 1) * gw + (q & 1)) * (int)h_row_bytes + cs * gemm::kRowB);
+      },
+      S, lw0, lw1, lx0, lx1);
+
+#pragma unroll
+  for (int ti = 0; ti < TW; ++ti) {
+    const int64_t n = (int64_t)t0 + tg * 32 * TW + ti * 32 + col;
+    if (n >= Ntot) continue;
+#pragma unroll
+    for (int fi = 0; fi < 4; ++fi) {
+      const int fb = f0 + 128 * hh + 32 * fi;
+      if (fb >= D) continue;
+      float* orow = tokens + n * D + fb;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int f = fb + rg * 8 + 4 * hl;
+        const float4 bb = *reinterpret_cast<const float4*>(b2 + f);
+        const float4 cc = *reinterpret_cast<const float4*>(cond + f);
+        float4 o;
+        o.x = acc[ti][fi][rg * 4 + 0] + bb.x + cc.x;
+        o.y = acc[ti][fi][rg * 4 + 1] + bb.y + cc.y;
+        o.z = acc[ti][fi][rg * 4 + 2] + bb.z + cc.z;
+        o.w = acc[ti][fi][rg * 4 + 3] + bb.w + cc.w;
+        *reinterpret_cast<float4*>(orow + rg * 8 + 4 * hl) = o;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void merge_gemm_kernel(
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ w2, const float* __restrict__ b2,
+    const float* __restrict__ cond, int64_t Ntot, int Nimg, int tw, int gw, int64_t P, int C1,
+    int D, uint32_t h_bytes, int S, gemm::Plan plan, float* __restrict__ tokens) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lw0[gemm::kWTileB], lw1[gemm::kWTileB],
+      lx0[gemm::kXTileB], lx1[gemm::kXTileB];
+  const gemm::Tile tl = gemm::tile_of(blockIdx.x, plan);
+  if (tl.full)
+    merge_tile<2>(h, w2, b2, cond, Ntot, Nimg, tw, gw, P, C1, D, h_bytes, S, tl.f0, tl.t0, tokens,
+                  lw0, lw1, lx0, lx1);
+  else
+    merge_tile<1>(h, w2, b2, cond, Ntot, Nimg, tw, gw, P, C1, D, h_bytes, S, tl.f0, tl.t0, tokens,
+                  lw0, lw1, lx0, lx1);
+}
+
+}  // namespace
+
+hipError_t launch_gen_patchify(const float* z, int B, int H, int W, void* patches,
+                               hipStream_t stream) {
+  const int gw = W / kPatch;
+  const int64_t items = (int64_t)B * 3 * H * gw;
+  if (items == 0) return hipSuccess;
+  const int64_t P = (int64_t)(H / kPatch) * gw;
+  hipLaunchKernelGGL(patchify_bf16_kernel, dim3((unsigned)stream_grid(items)),
+                     dim3(kStreamThreads), 0, stream, z, items, H, gw, P,
+                     static_cast<uint16_t*>(patches));
+  return hipGetLastError();
+}
+
+hipError_t launch_gen_patch_embed(const void* patches, int B, int H, int W, const void* w1,
+                                  const float* b1, int C1, double theta, void* h,
+                                  hipStream_t stream) {
+  const int gw = W / kPatch;
+  const int P = (H / kPatch) * gw;
+  const int64_t M = (int64_t)B * P;
+  if (M == 0) return hipSuccess;
+  const gemm::Plan plan = gemm::make_plan(C1, M);
+  // pair i of a half of width C1/2 turns at theta^(-2i/(C1/2)) = 2^(-i l2f)
+  const float l2f = (float)(2.0 * log2(theta) / (C1 / 2));
+  hipLaunchKernelGGL(patch_gemm_kernel, dim3((unsigned)(plan.n_full + plan.n_half)),
+                     dim3(kThreads), 0, stream, static_cast<const uint16_t*>(patches),
+                     static_cast<const uint16_t*>(w1), b1, M, C1, gw, P, l2f, plan,
+                     static_cast<uint16_t*>(h));
+  return hipGetLastError();
+}
+
+hipError_t launch_gen_cond_hidden(float arg_t, float arg_s, int D, const void* wa_t,
+                                  const float* ba_t, const void* wa_s, const float* ba_s,
+                                  float* hidden, hipStream_t stream) {
+  const int64_t rows = 2 * (int64_t)D;
+  const int per = kStreamThreads / 64;
+  hipLaunchKernelGGL(cond_hidden_kernel, dim3((unsigned)((rows + per - 1) / per)),
+                     dim3(kStreamThreads), 0, stream, arg_t, arg_s, D,
+                     static_cast<const uint16_t*>(wa_t), ba_t, static_cast<const uint16_t*>(wa_s),
+                     ba_s, hidden);
+  return hipGetLastError();
+}
+
+hipError_t launch_gen_cond_out(int D, const float* hidden, const void* wb_t, const float* bb_t,
+                               const void* wb_s, const float* bb_s, float* cond,
+                               hipStream_t stream) {
+  const int per = kStreamThreads / 64;
+  hipLaunchKernelGGL(cond_out_kernel, dim3((unsigned)((D + per - 1) / per)), dim3(kStreamThreads),
+                     0, stream, D, hidden, static_cast<const uint16_t*>(wb_t), bb_t,
+                     static_cast<const uint16_t*>(wb_s), bb_s, cond);
+  return hipGetLastError();
+}
+
+hipError_t launch_gen_merge_embed(const void* h, int B, int H, int W, int C1, const void* w2,
+                                  const float* b2, const float* cond, int D, float* tokens,
+                                  hipStream_t stream) {
+  const int gw = W / kPatch, tw = W / (2 * kPatch);
+  const int Nimg = (H / (2 * kPatch)) * tw;
+  const int64_t Ntot = (int64_t)B * Nimg;
+  if (Ntot == 0) return hipSuccess;
+  const int64_t P = (int64_t)(H / kPatch) * gw;
+  const uint32_t h_bytes = (uint32_t)((int64_t)B * P * C1 * 2);
+  const gemm::Plan plan = gemm::make_plan(D, Ntot);
+  hipLaunchKernelGGL(merge_gemm_kernel, dim3((unsigned)(plan.n_full + plan.n_half)),
+                     dim3(kThreads), 0, stream, static_cast<const uint16_t*>(h),
+                     static_cast<const uint16_t*>(w2), b2, cond, Ntot, Nimg, tw, gw, P, C1, D,
+                     h_bytes, 4 * C1 / gemm::kKS, plan, tokens);
+  return hipGetLastError();
+}
+
+}  // namespace neo

@@ -10,11 +10,12 @@ namespace neo {
 constexpr int kHeadDim = 128;
 constexpr int kHalfDim = 64;
 
-// threads per workgroup of the attention (bf16 / fp32) and projection launches; a launch's
-// work-items (workgroups x threads) must fit the dispatch's 32-bit grid size
+// threads per workgroup of the attention (bf16 / fp32) and matrix-product (projection,
+// front-end convolution) launches; a launch's work-items (workgroups x threads) must fit
+// the dispatch's 32-bit grid size
 constexpr int kAttnBf16Threads = 512;
 constexpr int kAttnF32Threads = 256;
-constexpr int kProjThreads = 512;
+constexpr int kGemmThreads = 512;
 
 // ---- launchers (host side); each returns the hipError_t of its launch --------------
 
@@ -46,6 +47,25 @@ hipError_t launch_qkv_proj_bf16(const void* x, const void* w, int64_t N, int hid
                                 const float* wk_hw, const int32_t* pos, double theta,
                                 double theta_hw, float eps, void* q_out, void* k_out,
                                 void* v_out, hipStream_t stream);
+
+// upper bound of the workgroups a matrix-product launch uses for F features by T tokens
+inline int64_t gemm_max_blocks(int64_t F, int64_t T) { return 2 * ((F + 255) / 256) * ((T + 255) / 256); }
+
+// generation-branch embedding front end
+hipError_t launch_gen_patchify(const float* z, int B, int H, int W, void* patches,
+                               hipStream_t stream);
+hipError_t launch_gen_patch_embed(const void* patches, int B, int H, int W, const void* w1,
+                                  const float* b1, int C1, double theta, void* h,
+                                  hipStream_t stream);
+hipError_t launch_gen_cond_hidden(float arg_t, float arg_s, int D, const void* wa_t,
+                                  const float* ba_t, const void* wa_s, const float* ba_s,
+                                  float* hidden, hipStream_t stream);
+hipError_t launch_gen_cond_out(int D, const float* hidden, const void* wb_t, const float* bb_t,
+                               const void* wb_s, const float* bb_s, float* cond,
+                               hipStream_t stream);
+hipError_t launch_gen_merge_embed(const void* h, int B, int H, int W, int C1, const void* w2,
+                                  const float* b2, const float* cond, int D, float* tokens,
+                                  hipStream_t stream);
 
 hipError_t launch_euler_step(float* z, const float* x0, int64_t n, float coef,
                              hipStream_t stream);

@@ -277,3 +277,79 @@ def test_proj_validation(L, kw, status):
 
 def test_proj_empty_is_ok(L):
     assert _proj(L, N=0, x=None) == P.NEO_OK
+
+
+# ---- embedding front end: host-side validation (nothing is launched) ------------------------
+
+def _fe(L, fn, **kw):
+    d = dict(z=FAKE, B=1, H=512, Wd=512, p=FAKE + (1 << 30), w1=FAKE + (2 << 30),
+             b1=FAKE + (3 << 30), C1=1024, th=1e4, h=FAKE + (4 << 30), t=0.5, ns=2.0, nsm=16.0,
+             D=4096, wa_t=FAKE + (5 << 30), ba_t=FAKE + (6 << 30), wa_s=FAKE + (7 << 30),
+             ba_s=FAKE + (8 << 30), hid=FAKE + (9 << 30), wb_t=FAKE + (10 << 30),
+             bb_t=FAKE + (11 << 30), wb_s=FAKE + (12 << 30), bb_s=FAKE + (13 << 30),
+             cond=FAKE + (14 << 30), w2=FAKE + (15 << 30), b2=FAKE + (16 << 30),
+             tok=FAKE + (17 << 30))
+    d.update(kw)
+    if fn == "patchify":
+        return L.neo_gen_patchify(d["z"], d["B"], d["H"], d["Wd"], d["p"], None)
+    if fn == "patch":
+        return L.neo_gen_patch_embed(d["p"], d["B"], d["H"], d["Wd"], d["w1"], d["b1"], d["C1"],
+                                     d["th"], d["h"], None)
+    if fn == "hidden":
+        return L.neo_gen_cond_hidden(d["t"], d["ns"], d["nsm"], d["D"], d["wa_t"], d["ba_t"],
+                                     d["wa_s"], d["ba_s"], d["hid"], None)
+    if fn == "out":
+        return L.neo_gen_cond_out(d["D"], d["hid"], d["wb_t"], d["bb_t"], d["wb_s"], d["bb_s"],
+                                  d["cond"], None)
+    return L.neo_gen_merge_embed(d["h"], d["B"], d["H"], d["Wd"], d["C1"], d["w2"], d["b2"],
+                                 d["cond"], d["D"], d["tok"], None)
+
+
+@pytest.mark.parametrize("fn,kw,status", [
+    ("patchify", dict(H=520), P.NEO_ERR_SHAPE),                 # not a multiple of 16
+    ("patchify", dict(Wd=0), P.NEO_ERR_SHAPE),
+    ("patchify", dict(B=-1), P.NEO_ERR_SHAPE),
+    ("patchify", dict(H=1 << 16), P.NEO_ERR_SHAPE),
+    ("patchify", dict(z=None), P.NEO_ERR_NULL),
+    ("patchify", dict(p=FAKE + 8), P.NEO_ERR_VALUE),              # misaligned
+    ("patchify", dict(p=FAKE + 4096), P.NEO_ERR_VALUE),           # patches overlap z
+    ("patch", dict(C1=100), P.NEO_ERR_SHAPE),                   # not a multiple of 64
+    ("patch", dict(C1=0), P.NEO_ERR_SHAPE),
+    ("patch", dict(H=40), P.NEO_ERR_SHAPE),
+    ("patch", dict(th=1.0), P.NEO_ERR_VALUE),
+    ("patch", dict(th=math.inf), P.NEO_ERR_VALUE),
+    ("patch", dict(b1=None), P.NEO_ERR_NULL),
+    ("patch", dict(h=FAKE + (1 << 30) + 64), P.NEO_ERR_VALUE),   # h overlaps the patches
+    ("patch", dict(B=1 << 16, H=1 << 15, Wd=1 << 15), P.NEO_ERR_SHAPE),  # grid too large
+    ("hidden", dict(D=100), P.NEO_ERR_SHAPE),                   # not a multiple of 8
+    ("hidden", dict(nsm=0.0), P.NEO_ERR_VALUE),
+    ("hidden", dict(t=math.nan), P.NEO_ERR_VALUE),
+    ("hidden", dict(wa_s=None), P.NEO_ERR_NULL),
+    ("hidden", dict(hid=FAKE + (5 << 30) + 128), P.NEO_ERR_VALUE),  # hidden inside wa_t
+    ("out", dict(D=0), P.NEO_ERR_SHAPE),
+    ("out", dict(bb_s=None), P.NEO_ERR_NULL),
+    ("out", dict(cond=FAKE + (9 << 30)), P.NEO_ERR_VALUE),      # cond overlaps hidden
+    ("out", dict(wb_t=FAKE + (10 << 30) + 4), P.NEO_ERR_VALUE),  # misaligned
+    ("merge", dict(H=48), P.NEO_ERR_SHAPE),                     # not a multiple of 32
+    ("merge", dict(D=48), P.NEO_ERR_SHAPE),                     # not a multiple of 32
+    ("merge", dict(C1=96), P.NEO_ERR_SHAPE),
+    ("merge", dict(B=4, H=8192, Wd=8192), P.NEO_ERR_SHAPE),      # features reach 2 GiB
+    ("merge", dict(cond=None), P.NEO_ERR_NULL),
+    ("merge", dict(tok=FAKE + (16 << 30)), P.NEO_ERR_VALUE),     # tokens overlap b2
+])
+def test_front_end_validation(L, fn, kw, status):
+    assert _fe(L, fn, **kw) == status
+    assert L.neo_last_error().decode().startswith("neo_gen_")
+
+
+def test_front_end_empty_is_ok(L):
+    assert _fe(L, "patchify", B=0, z=None) == P.NEO_OK
+    assert _fe(L, "patch", B=0, p=None) == P.NEO_OK
+    assert _fe(L, "merge", B=0, h=None) == P.NEO_OK
+
+
+def test_shift_time_matches_oracle(L):
+    from oracle import front_end as fe
+    for t in np.linspace(0.0, 1.0, 17):
+        for s in (0.5, 1.0, 3.0, 6.0):
+            assert P.shift_time(t, s) == pytest.approx(fe.shift_time(t, s), abs=1e-15)
