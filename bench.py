@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--proj-steps", type=int, default=50,
                     help="timed calls of the fused q/k/v projection + prologue on the workload's "
                          "image tokens, beside a library GEMM plus the separate prologue (0 skips)")
+    ap.add_argument("--embed-steps", type=int, default=50,
+                    help="calls per kernel of the embedding front end at the workload's pixels")
     ap.add_argument("--prefill-steps", type=int, default=100,
                     help="timed calls of the block-causal prefill attention on the editing "
                          "workload's prefixes (0 skips it)")
@@ -61,10 +63,12 @@ def parse():
     return ap.parse_args()
 
 
-KERNELS = {"gen_attn_bf16_kernel": "gen_attn_bf16_kernel", "qknorm_rope3": "qknorm_rope3_kernel",
+KERNELS = {"patch_gemm_kernel": "patch_gemm_kernel", "merge_gemm_kernel": "merge_gemm_kernel",
+           "gen_attn_bf16_kernel": "gen_attn_bf16_kernel", "qknorm_rope3": "qknorm_rope3_kernel",
            "fm_euler_step": "euler_vec4_kernel", "prefill_attn_bf16_kernel": "prefill_attn_bf16_kernel",
            "fm_euler_step_cfg": "euler_cfg_vec4_kernel", "qkv_proj_bf16_kernel": "qkv_proj_bf16_kernel"}
-KERNEL_SOURCES = {"gen_attn_bf16_kernel": "gen_attn.hip", "qknorm_rope3": "qknorm_rope3.hip",
+KERNEL_SOURCES = {"patch_gemm_kernel": "front_end.hip", "merge_gemm_kernel": "front_end.hip",
+                  "gen_attn_bf16_kernel": "gen_attn.hip", "qknorm_rope3": "qknorm_rope3.hip",
                   "fm_euler_step": "euler_step.hip", "prefill_attn_bf16_kernel": "gen_attn.hip",
                   "fm_euler_step_cfg": "euler_step.hip", "qkv_proj_bf16_kernel": "qkv_proj.hip"}
 
@@ -115,6 +119,23 @@ def derive_traffic(a):
     with open(a.traffic_json, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
+
+
+def timed_calls(fn, n):
+    """Mean duration in us of n calls of fn, each bracketed by its own pair of events on the
+    current stream (after 5 untimed calls)."""
+    import torch
+    for _ in range(5):
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
 
 
 def measured_bytes(a, key):
@@ -332,20 +353,8 @@ def main():
                              y[:, nq:nq + nk].view(w.Tq, w.Hkv, 128).contiguous(), *nws,
                              shared["pos"], w.rope_theta, w.rope_theta_hw, w.eps)
 
-        def timed(fn):
-            for _ in range(5):
-                fn()
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(a.proj_steps)]
-            torch.cuda.synchronize()
-            for e0, e1 in evs:
-                e0.record()
-                fn()
-                e1.record()
-            torch.cuda.synchronize()
-            return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
-        us = timed(fused)
-        us_lib = timed(unfused)
+        us = timed_calls(fused, a.proj_steps)
+        us_lib = timed_calls(unfused, a.proj_steps)
         proj = {"workload": f"{w.Tq} tokens x hidden {hid} -> {w.Hq}+{w.Hkv}+{w.Hkv} heads",
                 "gflop": pflops / 1e9, "us": us, "tflops": pflops / (us * 1e-6) / 1e12,
                 "frac": pflops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
@@ -353,6 +362,60 @@ def main():
                 "hbm_bytes_measured": measured_bytes(a, "qkv_proj_bf16_kernel")}
         del px, pw, pq, pk, pv, y
         print(f"[bench] fused projection timed ({a.proj_steps} calls)", file=sys.stderr, flush=True)
+
+    # the generation branch's embedding front end at the workload's pixel shape: patchify,
+    # patch convolution (+ GELU + rotary), the two embedders, the merge convolution
+    embed = {}
+    if a.embed_steps > 0:
+        d = W.embed_inputs(w)
+        r = W.bf16_round
+        Bz, _, Hz, Wz = d["z"].shape
+        C1, D = d["w1"].shape[0], d["w2"].shape[0]
+        ez = H.dev_f32(d["z"])
+        ew1 = H.dev(r(d["w1"]).reshape(C1, -1), "bf16")
+        eb1, eb2 = H.dev_f32(d["b1"]), H.dev_f32(d["b2"])
+        ew2 = H.dev(np.ascontiguousarray(r(d["w2"]).transpose(0, 2, 3, 1)), "bf16")
+        embs = [(H.dev(r(e[0]), "bf16"), H.dev_f32(e[1]), H.dev(r(e[2]), "bf16"), H.dev_f32(e[3]))
+                for e in (d["emb_t"], d["emb_s"])]
+        del d["w2"], d["emb_t"], d["emb_s"]
+        npix, P = Bz * 3 * Hz * Wz, Bz * (Hz // 16) * (Wz // 16)
+        ntok = Bz * (Hz // 32) * (Wz // 32)
+        pbuf = torch.empty((P, 768), dtype=torch.bfloat16, device=dev)
+        hbuf = torch.empty((P, C1), dtype=torch.bfloat16, device=dev)
+        hid = torch.empty((2, D), dtype=torch.float32, device=dev)
+        cbuf = torch.empty((D,), dtype=torch.float32, device=dev)
+        tbuf = torch.empty((ntok, D), dtype=torch.float32, device=dev)
+        us_p = timed_calls(lambda: neo.gen_patchify(ez, patches=pbuf), a.embed_steps)
+        us_c = timed_calls(lambda: neo.gen_patch_embed(pbuf, Bz, Hz, Wz, ew1, eb1, h_out=hbuf),
+                           a.embed_steps)
+        us_e = timed_calls(lambda: neo.gen_cond_embed(d["t"], d["noise_scale"], d["noise_scale_max"],
+                                                      embs[0], embs[1], hidden=hid, cond=cbuf),
+                           a.embed_steps)
+        us_m = timed_calls(lambda: neo.gen_merge_embed(hbuf, Bz, Hz, Wz, ew2, eb2, cbuf, tokens=tbuf),
+                           a.embed_steps)
+        # a library matrix product of the merge's shape (contiguous operands), for scale
+        ga = torch.empty((ntok, 4 * C1), dtype=torch.bfloat16, device=dev).normal_()
+        gy = torch.empty((ntok, D), dtype=torch.bfloat16, device=dev)
+        us_lib = timed_calls(lambda: torch.matmul(ga, ew2.view(D, -1).t(), out=gy), a.embed_steps)
+        p_bytes = npix * 6                                   # fp32 read + bf16 written
+        c_flop = 2.0 * P * C1 * 768
+        e_bytes = 2 * D * 256 * 2 + 2 * D * D * 2           # both layers' bf16 weights
+        m_flop = 2.0 * ntok * D * 4 * C1
+        embed = {
+            "workload": f"{Bz}x3x{Hz}x{Wz} px -> {ntok} tokens, C1={C1}, D={D}",
+            "patchify": {"us": us_p, "bytes": p_bytes, "gbs": p_bytes / (us_p * 1e-6) / 1e9},
+            "patch_conv_gelu_rope": {"us": us_c, "gflop": c_flop / 1e9,
+                                     "tflops": c_flop / (us_c * 1e-6) / 1e12,
+                                     "frac": c_flop / (us_c * 1e-6) / 1e12 / PEAK_BF16_TFLOPS},
+            "cond_embedders": {"us": us_e, "bytes": e_bytes, "gbs": e_bytes / (us_e * 1e-6) / 1e9},
+            "merge_conv": {"us": us_m, "gflop": m_flop / 1e9, "tflops": m_flop / (us_m * 1e-6) / 1e12,
+                           "frac": m_flop / (us_m * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+                           "library_gemm_same_shape_us": us_lib},
+            "total_us": us_p + us_c + us_e + us_m,
+        }
+        del ez, ew1, ew2, embs, pbuf, hbuf, tbuf, ga, gy
+        print(f"[bench] embedding front end timed ({a.embed_steps} calls per kernel)",
+              file=sys.stderr, flush=True)
 
     # the understanding-pass (prefill) attention of the next row, on the editing workload's
     # four ragged prefixes (text, a 1024-token reference image, suffix)
@@ -433,6 +496,7 @@ def main():
         "cfg_euler": cfg,
         "prefill_attention": prefill,
         "qkv_projection": proj,
+        "embedding_front_end": embed,
     }
     print(json.dumps(result), flush=True)
 
