@@ -459,7 +459,13 @@ __device__ __forceinline__ void attn_bf16_body(
         // the matrix products of early slots rather than right after the barrier
         if (k == kLoadSlotK && kmore) load_k(T + 2, bm1);
         if (k == kLoadSlotV && vmore) load_v(T + 1, b1);
+        // the weights of the slot run at raised wave priority: when both waves of a SIMD
+        // are ready, the softmax of one is issued first and the matrix products of the
+        // other fill the gap (measured ~2% faster than equal priority; raising it around
+        // the products instead gains nothing)
+        __builtin_amdgcn_s_setprio(1);
         exp_pair(scur, i, pk, tsum);
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
         if (i == 7) finish_step(2 * T + h, scur, snext, pcur, pk, tsum);
       }
