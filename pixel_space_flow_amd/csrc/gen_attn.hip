@@ -459,10 +459,11 @@ __device__ __forceinline__ void attn_bf16_body(
         // the matrix products of early slots rather than right after the barrier
         if (k == kLoadSlotK && kmore) load_k(T + 2, bm1);
         if (k == kLoadSlotV && vmore) load_v(T + 1, b1);
-        // the weights of the slot run at raised wave priority: when both waves of a SIMD
-        // are ready, the softmax of one is issued first and the matrix products of the
-        // other fill the gap (measured ~2% faster than equal priority; raising it around
-        // the products instead gains nothing)
+        // the weights of the slot are bracketed by a raised-priority window.  The weights are
+        // pure values that the compiler mostly schedules outside the window, so it seldom
+        // holds the exponentials, but the markers shift the slot's schedule: measured ~2%
+        // faster than without them in same-box A/B.  A window around the products instead
+        // gained nothing, and pinning the weights inside the window was ~4% slower.
         __builtin_amdgcn_s_setprio(1);
         exp_pair(scur, i, pk, tsum);
         __builtin_amdgcn_s_setprio(0);
