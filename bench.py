@@ -194,7 +194,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the block shards by KV head or by CFG branch with no exchange inside it). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
