@@ -132,41 +132,51 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope3_kernel(
         sincospif((float)(2.0 * rev), &sn[e], &cs[e]);
       }
     }
-    for (int r0 = 0; r0 < rows; r0 += 4) {
-      const int r = r0 + grp;
-      const bool valid = r < rows;
-      const bool is_q = r < Hq;
-      float x[8];
-      if (valid) {
-        if (is_q)
-          RowIO<kBf16>::load(q_in, t * Hq + r, sub, x);
-        else
-          RowIO<kBf16>::load(k_in, t * Hkv + (r - Hq), sub, x);
-      } else {
+    // rows in batches of 16 (four per 16-lane group): the batch's loads are all issued
+    // before its first store, so four loads per lane are in flight (each row is still
+    // loaded before it is stored, which keeps the in-place call correct)
+    for (int r0 = 0; r0 < rows; r0 += 16) {
+      float x[4][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+      for (int gi = 0; gi < 4; ++gi) {
+        const int r = r0 + 4 * gi + grp;
+        if (r < rows) {
+          if (r < Hq)
+            RowIO<kBf16>::load(q_in, t * Hq + r, sub, x[gi]);
+          else
+            RowIO<kBf16>::load(k_in, t * Hkv + (r - Hq), sub, x[gi]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[gi][e] = 0.0f;
+        }
       }
-      float ss = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
-      ss += __shfl_xor(ss, 1);
-      ss += __shfl_xor(ss, 2);
-      ss += __shfl_xor(ss, 4);
-      const float rinv = rsqrtf(ss * (1.0f / kHalfDim) + eps);
-      float y[8];
+      for (int gi = 0; gi < 4; ++gi) {
+        const int r = r0 + 4 * gi + grp;
+        const bool valid = r < rows;
+        const bool is_q = r < Hq;
+        float ss = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = x[e] * rinv * (is_q ? wq[e] : wk[e]);
-      float out[8];
+        for (int e = 0; e < 8; ++e) ss = fmaf(x[gi][e], x[gi][e], ss);
+        ss += __shfl_xor(ss, 1);
+        ss += __shfl_xor(ss, 2);
+        ss += __shfl_xor(ss, 4);
+        const float rinv = rsqrtf(ss * (1.0f / kHalfDim) + eps);
+        float y[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float yp = __shfl_xor(y[e], partner_xor);
-        out[e] = fmaf(y[e], cs[e], sgn * yp * sn[e]);
-      }
-      if (valid) {
-        if (is_q)
-          RowIO<kBf16>::store(q_out, t * Hq + r, sub, out);
-        else
-          RowIO<kBf16>::store(k_out, t * Hkv + (r - Hq), sub, out);
+        for (int e = 0; e < 8; ++e) y[e] = x[gi][e] * rinv * (is_q ? wq[e] : wk[e]);
+        float out[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float yp = __shfl_xor(y[e], partner_xor);
+          out[e] = fmaf(y[e], cs[e], sgn * yp * sn[e]);
+        }
+        if (valid) {
+          if (is_q)
+            RowIO<kBf16>::store(q_out, t * Hq + r, sub, out);
+          else
+            RowIO<kBf16>::store(k_out, t * Hkv + (r - Hq), sub, out);
+        }
       }
     }
   }
