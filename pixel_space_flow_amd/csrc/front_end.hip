@@ -156,15 +156,13 @@ __device__ __forceinline__ void patch_tile(const uint16_t* __restrict__ patches,
           v[e] = gelu(x);
         }
         // pairs (f, f + 1), f even: elements e = 0, 1 and 2, 3.  The angle is taken in
-        // revolutions and reduced by the nearest whole turn before sincospif, which needs no
-        // wide argument reduction (positions are below 2^11, so the fp32 revolutions carry
-        // an absolute error under 1e-4 turn at the largest image and ~1e-6 at 2048 px).
+        // revolutions and reduced to quarter turns inside sincos_turns, which needs no wide
+        // argument reduction (positions are below 2^11, so the fp32 revolutions carry an
+        // absolute error under 1e-4 turn at the largest image and ~1e-6 at 2048 px).
 #pragma unroll
         for (int e = 0; e < 4; e += 2) {
-          float rev = pos * rate[fi][rg][e >> 1];
-          rev -= rintf(rev);
           float sn, cs;
-          sincospif(2.0f * rev, &sn, &cs);
+          sincos_turns(pos * rate[fi][rg][e >> 1], &sn, &cs);
           const float a = v[e], b = v[e + 1];
           v[e] = a * cs - b * sn;
           v[e + 1] = a * sn + b * cs;

@@ -105,7 +105,7 @@ __device__ __forceinline__ void proj_tile(
     auto angle = [&](double p, double freq, float& sn, float& cs) __attribute__((always_inline)) {
       double rev = p * freq * kInv2Pi;
       rev -= rint(rev);  // exact: the angle modulo one turn, in [-1/2, 1/2]
-      sincospif((float)(2.0 * rev), &sn, &cs);
+      sincos_turns((float)rev, &sn, &cs);
     };
     {
       // temporal slice: dims [0, 64), pairs (i, i + 32); i = row(r) in accumulator 0
