@@ -125,14 +125,25 @@ __device__ __forceinline__ int sub_valid(const Segments& S, int s) {
 
 // Last position of the run of equal temporal indices that contains position `start`
 // (within a sample the indices are non-decreasing and equal ones are contiguous).  All
-// lanes of the wave call it with the same arguments; 64 positions per probe.
+// lanes of the wave call it with the same arguments.  A probe covers 1024 positions:
+// lane L reads positions base + 64 j + L for j < 16 (16 coalesced loads, all issued before
+// any is examined), so a run of up to 1024 positions -- a whole image block -- costs one
+// memory round trip rather than one per 64 positions.
 __device__ __forceinline__ int run_end(const int32_t* ix, int start, int n, int lane) {
   const int v0 = ix[start];
-  for (int base = start + 1; base < n; base += 64) {
-    const int p = base + lane;
-    const bool differs = p >= n || ix[p] != v0;  // no read at or past n
-    const uint64_t bal = __ballot(differs);
-    if (bal != 0) return base + (int)__builtin_ctzll(bal) - 1;
+  for (int base = start + 1; base < n; base += 1024) {
+    int v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int p = base + 64 * j + lane;
+      v[j] = p < n ? ix[p] : 0;  // no read at or past n
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int p = base + 64 * j + lane;
+      const uint64_t bal = __ballot(p >= n || v[j] != v0);
+      if (bal != 0) return base + 64 * j + (int)__builtin_ctzll(bal) - 1;
+    }
   }
   return n - 1;
 }
@@ -197,13 +208,17 @@ __device__ __forceinline__ void attn_bf16_body(
   const bool qvalid = active && qi < N;
 
   // prefill: the keys the workgroup's queries may see are 0 .. kmax-1; lane_lim is the
-  // number of keys this lane's query may see, lim_min the smallest over the wave
+  // number of keys this lane's query may see, lim_min the smallest over the wave.  They are
+  // found after the first tile loads are issued (prefill_limits below), so the probes of
+  // the temporal indices overlap those loads.
   int kmax = N, lane_lim = 1 << 30, lim_min = 1 << 30;
-  if constexpr (kPrefill) {
+  auto prefill_limits = [&]() __attribute__((always_inline)) {
     const int32_t* ix = tidx + qa;
     const int last_c = (cg * kWaves + kWaves < nchunks ? cg * kWaves + kWaves : nchunks) - 1;
     const int wg_last = ((last_c / G) * 32 + 32 < N ? (last_c / G) * 32 + 32 : N) - 1;
-    kmax = run_end(ix, wg_last, N, lane) + 1;
+    // wave-uniform by construction; readfirstlane tells the compiler, so the key range and
+    // every per-tile condition derived from it stay scalar
+    kmax = __builtin_amdgcn_readfirstlane(run_end(ix, wg_last, N, lane) + 1);
     if (active) {
       const int t0 = (c / G) * 32;
       const int nq = N - t0 < 32 ? N - t0 : 32;
@@ -213,12 +228,15 @@ __device__ __forceinline__ void attn_bf16_body(
         const int im = __shfl(my, m);
         if (m > col && m < nq && e == m - 1 && im == my) e = m;
       }
-      const int wave_end = run_end(ix, t0 + nq - 1, N, lane);
+      // the wave's last query ends the same run as the workgroup's last one when their
+      // indices are equal (indices are non-decreasing), which spares the second probe
+      const int wave_last = t0 + nq - 1;
+      const int wave_end = ix[wave_last] == ix[wg_last] ? kmax - 1 : run_end(ix, wave_last, N, lane);
       lane_lim = (e == nq - 1 ? wave_end : t0 + e) + 1;
       if (!qvalid) lane_lim = kmax;
-      lim_min = __shfl(lane_lim, 0);
+      lim_min = __builtin_amdgcn_readfirstlane(lane_lim);  // lane 0's limit, the smallest
     }
-  }
+  };
 
   Segments S;
   S.row_bytes = (uint32_t)Hkv * kHeadDim * 2;
@@ -227,12 +245,13 @@ __device__ __forceinline__ void attn_bf16_body(
   S.vbase[0] = reinterpret_cast<const uint8_t*>(v_pre + (pa * Hkv + g) * kHeadDim);
   S.kbase[1] = reinterpret_cast<const uint8_t*>(k_img + (qa * Hkv + g) * kHeadDim);
   S.vbase[1] = reinterpret_cast<const uint8_t*>(v_img + (qa * Hkv + g) * kHeadDim);
+  // the image segment's rows bound the tile loads (the prefill cuts its key range at kmax
+  // through the tile count and masks keys past each lane's limit)
   S.len[0] = P;
-  S.len[1] = kmax;
+  S.len[1] = N;
   S.ntiles[0] = (P + kBN - 1) / kBN;
-  S.ntiles[1] = (kmax + kBN - 1) / kBN;
-  const int ntiles = S.ntiles[0] + S.ntiles[1];
-  const int nsub = 2 * ntiles;  // 32-key sub-tiles (trailing ones may be fully masked)
+  S.ntiles[1] = (N + kBN - 1) / kBN;
+  int ntiles = S.ntiles[0] + S.ntiles[1];  // the prefill recomputes it from kmax below
 
   // staging: wave w fills 1 KB blocks 2w and 2w+1 of each tile (rows 4*blk .. +3); lane
   // L of block blk lands in row 4*blk + L/16, slot L%16 and so fetches chunk
@@ -401,6 +420,10 @@ __device__ __forceinline__ void attn_bf16_body(
   load_k(0, 0);
   load_v(0, 0);
   if (ntiles > 1) load_k(1, 1);
+  if constexpr (kPrefill) {
+    prefill_limits();
+    ntiles = (kmax + kBN - 1) / kBN;
+  }
   for (int i = tid; i < kTileBytes / 16; i += kThreads)
     reinterpret_cast<uint4*>(lv2)[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
@@ -485,7 +508,7 @@ __device__ __forceinline__ void attn_bf16_body(
   }
   // last sub-tile's PV product (its P is in pb2)
   if (active) {
-    // sub-tile nsub-1 is the second half of tile ntiles-1
+    // the last sub-tile is the second half of tile ntiles-1
     const uint8_t* va = vbuf((ntiles - 1) % 3) + 32 * kRow;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
