@@ -87,11 +87,20 @@ def _counter_rows(d, counter):
 
 
 def _kernel_source_hash(key):
-    """sha256 of the HIP source a kernel is built from: byte counts taken from one build
-    are not reported for another."""
+    """sha256 of the HIP source a kernel is built from, followed by every header of the
+    library (the shared tile core and device helpers): byte counts taken from one build are
+    not reported for another."""
+    import glob
     import hashlib
-    with open(os.path.join(ROOT, "pixel_space_flow_amd", "csrc", KERNEL_SOURCES[key]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    csrc = os.path.join(ROOT, "pixel_space_flow_amd", "csrc")
+    files = [os.path.join(csrc, KERNEL_SOURCES[key])]
+    files += sorted(glob.glob(os.path.join(csrc, "*.h")))
+    files += [os.path.join(ROOT, "include", "neo.h")]
+    h = hashlib.sha256()
+    for path in files:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def derive_traffic(a):
