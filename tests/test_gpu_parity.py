@@ -496,6 +496,17 @@ def test_prefill_layouts(neo, layout):
     _prefill_case(neo, d, layout)
 
 
+def test_prefill_run_beyond_probe(neo):
+    """An image run of 2300 tokens: the kernel finds a run's end 1024 positions per probe,
+    so the workgroups whose last query lies early in the run need three probes.  The rows
+    compared cover every workgroup of the run (a stride) and both run boundaries."""
+    d = W.prefill_layout([[("text", 70), ("image", 2300), ("text", 40)]], 8, 2, seed=2300)
+    T = int(d["cu"][-1])
+    rows = np.array(sorted(set(range(0, T, 29)) | {0, 69, 70, 71, 1093, 1094, 2369, 2370,
+                                                    2371, T - 1}))
+    _prefill_case(neo, d, "run beyond one probe", rows=rows)
+
+
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (32, 4), (12, 4)])
 def test_prefill_heads(neo, hq, hkv):
     d = W.prefill_layout([[("text", 40), ("image", 70), ("text", 9)], [("text", 33)]], hq, hkv,
