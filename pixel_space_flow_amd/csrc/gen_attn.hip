@@ -211,7 +211,9 @@ __device__ __forceinline__ void attn_bf16_body(
   // number of keys this lane's query may see, lim_min the smallest over the wave.  They are
   // found after the first tile loads are issued (prefill_limits below), so the probes of
   // the temporal indices overlap those loads.
-  int kmax = N, lane_lim = 1 << 30, lim_min = 1 << 30;
+  // wave_tiles: the tiles any lane of this wave may see; past them the wave only stages
+  // tiles for the others (its scores would all be masked)
+  int kmax = N, lane_lim = 1 << 30, lim_min = 1 << 30, wave_tiles = 1 << 30;
   auto prefill_limits = [&]() __attribute__((always_inline)) {
     const int32_t* ix = tidx + qa;
     const int last_c = (cg * kWaves + kWaves < nchunks ? cg * kWaves + kWaves : nchunks) - 1;
@@ -223,11 +225,14 @@ __device__ __forceinline__ void attn_bf16_body(
       const int t0 = (c / G) * 32;
       const int nq = N - t0 < 32 ? N - t0 : 32;
       const int my = qvalid ? ix[qi] : 0;
-      int e = col;  // last query of the wave in this lane's run
-      for (int m = 1; m < 32; ++m) {
-        const int im = __shfl(my, m);
-        if (m > col && m < nq && e == m - 1 && im == my) e = m;
-      }
+      // e: the last query of the wave in this lane's run.  Runs are contiguous, so it is the
+      // first run boundary (query m with an index different from query m + 1's) at or after
+      // this lane's query, or the wave's last query if the run reaches it
+      const int next = __shfl(my, (lane & 32) | ((col + 1) & 31));
+      const uint32_t bounds =
+          (uint32_t)__ballot(col < nq - 1 && my != next);  // lanes 0..31 (one half suffices)
+      const uint32_t from_me = bounds >> col;
+      const int e = from_me != 0 ? col + __builtin_ctz(from_me) : nq - 1;
       // the wave's last query ends the same run as the workgroup's last one when their
       // indices are equal (indices are non-decreasing), which spares the second probe
       const int wave_last = t0 + nq - 1;
@@ -235,6 +240,9 @@ __device__ __forceinline__ void attn_bf16_body(
       lane_lim = (e == nq - 1 ? wave_end : t0 + e) + 1;
       if (!qvalid) lane_lim = kmax;
       lim_min = __builtin_amdgcn_readfirstlane(lane_lim);  // lane 0's limit, the smallest
+      // limits are non-decreasing along the wave: its last query sees the most keys
+      const int lim_max = __builtin_amdgcn_readlane(lane_lim, nq - 1);
+      wave_tiles = (lim_max + kBN - 1) / kBN;
     }
   };
 
@@ -432,6 +440,16 @@ __device__ __forceinline__ void attn_bf16_body(
   bf16x8 pa_[2], pb2[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) pb2[u] = as_bf16x8(make_uint4(0, 0, 0, 0));
+  // PV product of the last sub-tile a wave computed: the second half of the tile in V buffer
+  // vb, with its weights in pb2
+  auto pv_last = [&](int vb) {
+    const uint8_t* va = vbuf(vb) + 32 * kRow;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(va, i >> 2, i & 3), pb2[i >> 2],
+                                                         o[i & 3], 0, 0, 0);
+  };
+
   if (active) {
     sa = zero16;
 #pragma unroll
@@ -452,9 +470,12 @@ __device__ __forceinline__ void attn_bf16_body(
     constexpr int T3 = decltype(t3)::value;
     constexpr int b0 = T3, b1 = (T3 + 1) % 3, bm1 = (T3 + 2) % 3;
     const bool kmore = T + 2 < ntiles, vmore = T + 1 < ntiles;
-    if (!active) {
+    if (!active || T >= wave_tiles) {
       if (kmore) load_k(T + 2, bm1);
       if (vmore) load_v(T + 1, b1);
+      // a prefill wave whose keys end before the workgroup's: the PV product of its last
+      // sub-tile (second half of tile T - 1, still resident), which the next step would do
+      if (kPrefill && active && T == wave_tiles) pv_last(bm1);
     } else {
       uint32_t pk[2][4];
       float tsum = 0.0f;
@@ -506,15 +527,8 @@ __device__ __forceinline__ void attn_bf16_body(
     if (T + 2 >= ntiles) break;
     iteration(T + 2, C2{});
   }
-  // last sub-tile's PV product (its P is in pb2)
-  if (active) {
-    // the last sub-tile is the second half of tile ntiles-1
-    const uint8_t* va = vbuf((ntiles - 1) % 3) + 32 * kRow;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(va, i >> 2, i & 3), pb2[i >> 2],
-                                                         o[i & 3], 0, 0, 0);
-  }
+  // last sub-tile's PV product (its P is in pb2), for waves that ran to the last tile
+  if (active && wave_tiles >= ntiles) pv_last((ntiles - 1) % 3);
 
   const float ltot = lsum + __shfl_xor(lsum, 32);
   if (qvalid) {
