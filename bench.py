@@ -30,6 +30,9 @@ if ROOT not in sys.path:
 METRIC = "gen-pass attention TFLOP/s + image-tokens/s per FM step at 4096 tokens (1 GPU)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# decoder layers of the generation branch, each with its own norm + rotary and attention
+# ("SenseNova-U1.5 (NEO-unify) architecture", §Mixture of Transformers)
+N_LAYERS = 42
 
 
 def parse():
@@ -502,6 +505,14 @@ def main():
         "hbm_frac": {"qknorm_rope3": pro_gbs / PEAK_HBM_GBS, "fm_euler_step": eul_gbs / PEAK_HBM_GBS},
         "step_roofline": {"tokens_per_s_at_roofline": ntok / roof_step_s,
                           "frac": (ntok / gpu_step_s) / (ntok / roof_step_s)},
+        # the whole denoiser's share of this path: every layer's norm + rotary and attention
+        # (the layers' projections and MLPs are not part of it), then one Euler step
+        "model_shaped_step": {
+            "layers": N_LAYERS,
+            "us": (N_LAYERS * (float(pro_ms.mean()) + float(att_ms.mean()))
+                   + float(eul_ms.mean())) * 1e3,
+            "image_tokens_per_s": ntok / ((N_LAYERS * (float(pro_ms.mean()) + float(att_ms.mean()))
+                                           + float(eul_ms.mean())) * 1e-3)},
         "cfg_euler": cfg,
         "prefill_attention": prefill,
         "qkv_projection": proj,
