@@ -355,6 +355,57 @@ def test_attn_invariants():
     np.testing.assert_allclose(oracle.gen_attn(**swapped), ref, atol=1e-13)
 
 
+def test_attn_streaming_formulation_agrees():
+    """A second, independent fp64 formulation: streaming (online) softmax over keys in
+    blocks of 3, keeping a running maximum, a rescaled running sum and a rescaled running
+    output, the prefix keys first and then the image keys.  It must agree with the
+    oracle's two-pass evaluation to ~1e-12, output and log-sum-exp."""
+    rng = np.random.default_rng(15)
+    Hq, Hkv = 4, 2
+    a = _attn_inputs(rng, [9, 4], [7, 11], Hq, Hkv)
+    a["q"] *= 3.0  # spread the scores so the running maximum moves
+    out, lse = oracle.gen_attn(**a, with_lse=True)
+    scale = 1.0 / math.sqrt(128)
+    for b in range(2):
+        q0, q1 = a["cu_q"][b], a["cu_q"][b + 1]
+        p0, p1 = a["cu_p"][b], a["cu_p"][b + 1]
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            keys = [(a["k_pre"][j, g], a["v_pre"][j, g]) for j in range(p0, p1)]
+            keys += [(a["k_img"][j, g], a["v_img"][j, g]) for j in range(q0, q1)]
+            for i in range(q0, q1):
+                m, l, acc = -math.inf, 0.0, np.zeros(128)
+                for blk in range(0, len(keys), 3):
+                    s = [scale * float(a["q"][i, h] @ k_) for k_, _ in keys[blk:blk + 3]]
+                    m_new = max(m, max(s))
+                    c = math.exp(m - m_new)  # 0 on the first block
+                    l = l * c + sum(math.exp(x - m_new) for x in s)
+                    acc = acc * c + sum(math.exp(x - m_new) * v_ for x, (_, v_)
+                                        in zip(s, keys[blk:blk + 3]))
+                    m = m_new
+                np.testing.assert_allclose(out[i, h], acc / l, rtol=0, atol=1e-12)
+                assert abs(lse[i, h] - (m + math.log(l))) < 1e-12
+
+
+def test_attn_score_shift_invariance():
+    """Adding the same vector u to every key of a KV head adds q.u (times the scale) to all
+    of a query's scores: the output is unchanged and the log-sum-exp moves by exactly that
+    amount.  Catches a softmax without its normalisation and an lse taken before the
+    maximum is restored."""
+    rng = np.random.default_rng(16)
+    Hq, Hkv = 4, 2
+    a = _attn_inputs(rng, [6, 5], [3, 8], Hq, Hkv)
+    out, lse = oracle.gen_attn(**a, with_lse=True)
+    u = rng.standard_normal((Hkv, 128))
+    s = dict(a)
+    s["k_img"] = a["k_img"] + u[None]
+    s["k_pre"] = a["k_pre"] + u[None]
+    out_s, lse_s = oracle.gen_attn(**s, with_lse=True)
+    np.testing.assert_allclose(out_s, out, atol=1e-12)
+    shift = np.einsum("thd,hd->th", a["q"], np.repeat(u, Hq // Hkv, axis=0)) / math.sqrt(128)
+    np.testing.assert_allclose(lse_s - lse, shift, atol=1e-11)
+
+
 def test_attn_sampled_rows_match_full():
     """Evaluating a sampled set of query rows returns the same values as the full call."""
     rng = np.random.default_rng(14)
