@@ -202,7 +202,9 @@ neo_status neo_qkv_proj_norm_rope(const void *x, const void *w_qkv, int64_t N, i
  *                 rotary axis).  Precondition, not checked: within a sample the
  *                 indices are non-decreasing and tokens sharing an index are
  *                 contiguous, as in every layout the pages describe (text
- *                 tokens count up; an image's tokens share one index).
+ *                 tokens count up; an image's tokens share one index).  When
+ *                 it is broken the outputs are wrong, but every read stays
+ *                 within the sample's rows.
  *   cu_seqlens    [B+1] int32, device: sample s is rows [cu[s], cu[s+1]).
  *   max_seqlen    host-side bound on the sample lengths; total = T.
  *   softmax_scale <= 0 means 1/sqrt(128).
