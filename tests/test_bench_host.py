@@ -116,3 +116,18 @@ def test_source_hash_covers_the_headers(tmp_path, monkeypatch):
     (csrc / "gemm_tile.h").write_text("// tile core, edited")
     after = {k: b._kernel_source_hash(k) for k in b.KERNEL_SOURCES}
     assert all(before[k] != after[k] for k in before)
+
+
+def test_algorithmic_work_of_the_benchmark_workload():
+    """The per-launch work the roofline figures divide by, against their closed forms at
+    4096 image tokens, a 512-token prefix, 32/8 heads and 3 x 2048^2 pixels:
+    4 * 32 * 128 * 4096 * 4608 flops; 4096 tokens * (40 rows * 128 * 2 B read and written +
+    12 B of positions); 12 B per pixel."""
+    import workloads as W
+    b = _bench()
+    w = W.make("large", pixels=False)
+    flops, pro, euler, attn = b.algorithmic(w)
+    assert flops == 4 * 32 * 128 * 4096 * 4608 == pytest.approx(309.24e9, rel=1e-4)
+    assert pro == 4096 * (40 * 128 * 2 * 2 + 12) == pytest.approx(83.94e6, rel=1e-4)
+    assert euler == 3 * 2048 * 2048 * 12 == pytest.approx(150.99e6, rel=1e-4)
+    assert attn == (4096 * (32 + 8) * 2 + 512 * 8 * 2) * 128 * 2 == pytest.approx(85.98e6, rel=1e-4)
