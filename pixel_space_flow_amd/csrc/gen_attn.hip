@@ -531,18 +531,34 @@ __device__ __forceinline__ void attn_bf16_body(
   if (active && wave_tiles >= ntiles) pv_last((ntiles - 1) % 3);
 
   const float ltot = lsum + __shfl_xor(lsum, 32);
-  if (qvalid) {
-    const float inv = 1.0f / ltot;
-    uint16_t* orow = out + ((qa + qi) * Hq + h) * kHeadDim + 4 * hl;
+  // The output goes through LDS (free once every wave is past its last tile) so that each
+  // lane stores whole 16-byte chunks of 256-byte rows: wave w stages its 32 x 128 block in
+  // 8 KB of one former K/V buffer, row = query, chunk c of a row in slot c ^ (row % 16).
+  __syncthreads();
+  uint8_t* ob = ((wave >> 1) == 0 ? lk0 : (wave >> 1) == 1 ? lk1 : (wave >> 1) == 2 ? lk2 : lv0) +
+                (wave & 1) * 8192;
+  if (active) {
+    const float inv = qvalid ? 1.0f / ltot : 0.0f;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const uint32_t w0 = pack_bf16x2(o[db][rg * 4 + 0] * inv, o[db][rg * 4 + 1] * inv);
         const uint32_t w1 = pack_bf16x2(o[db][rg * 4 + 2] * inv, o[db][rg * 4 + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + db * 32 + rg * 8) = make_uint2(w0, w1);
+        const int slot = (db * 4 + rg) ^ (col & 15);
+        *reinterpret_cast<uint2*>(ob + col * 256 + slot * 16 + hl * 8) = make_uint2(w0, w1);
       }
-    if (lse != nullptr && hl == 0)
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's rows are in LDS
+    asm volatile("" ::: "memory");
+    const int q0 = qi - col;  // the wave's first query
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4), cch = lane & 15;
+      const uint4 vrow = *reinterpret_cast<const uint4*>(ob + r * 256 + ((cch ^ (r & 15)) * 16));
+      if (q0 + r < N)
+        *reinterpret_cast<uint4*>(out + ((qa + q0 + r) * Hq + h) * kHeadDim + cch * 8) = vrow;
+    }
+    if (qvalid && lse != nullptr && hl == 0)
       lse[(int64_t)h * Tq + qa + qi] = (m + __log2f(ltot)) * 0.69314718055994530942f;
   }
 }
