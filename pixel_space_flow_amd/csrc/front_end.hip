@@ -296,15 +296,20 @@ __device__ __forceinline__ void merge_tile(const uint16_t* __restrict__ h,
       },
       S, lw0, lw1, lx0, lx1);
 
+  // Each 32-token x 128-feature block goes out through LDS, so that every lane stores a
+  // whole 16-byte chunk and each half-wave a complete 512-byte row segment.  The tile
+  // buffers are free (the main loop ends with a barrier after its last fragment read).
+  // Wave w stages in its own 16 KB: row = token, 16-byte chunk c of a row in slot
+  // c ^ (row mod 32).
+  uint8_t* ob = ((wave >> 1) == 0 ? lw0 : (wave >> 1) == 1 ? lw1 : (wave >> 1) == 2 ? lx0 : lx1) +
+                (wave & 1) * 16384;
+  const int fw = f0 + 128 * hh;  // the wave's first feature
 #pragma unroll
   for (int ti = 0; ti < TW; ++ti) {
-    const int64_t n = (int64_t)t0 + tg * 32 * TW + ti * 32 + col;
-    if (n >= Ntot) continue;
 #pragma unroll
     for (int fi = 0; fi < 4; ++fi) {
-      const int fb = f0 + 128 * hh + 32 * fi;
+      const int fb = fw + 32 * fi;
       if (fb >= D) continue;
-      float* orow = tokens + n * D + fb;
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int f = fb + rg * 8 + 4 * hl;
@@ -315,9 +320,21 @@ __device__ __forceinline__ void merge_tile(const uint16_t* __restrict__ h,
         o.y = acc[ti][fi][rg * 4 + 1] + bb.y + cc.y;
         o.z = acc[ti][fi][rg * 4 + 2] + bb.z + cc.z;
         o.w = acc[ti][fi][rg * 4 + 3] + bb.w + cc.w;
-        *reinterpret_cast<float4*>(orow + rg * 8 + 4 * hl) = o;
+        const int slot = (8 * fi + 2 * rg + hl) ^ col;
+        *reinterpret_cast<float4*>(ob + col * 512 + slot * 16) = o;
       }
     }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the block is in LDS
+    asm volatile("" ::: "memory");
+    const int64_t nb = (int64_t)t0 + tg * 32 * TW + ti * 32;  // first token of the block
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 2 * i + (lane >> 5), c = lane & 31;
+      const float4 v = *reinterpret_cast<const float4*>(ob + r * 512 + ((c ^ r) * 16));
+      if (nb + r < Ntot && fw + 4 * c < D)
+        *reinterpret_cast<float4*>(tokens + (nb + r) * D + fw + 4 * c) = v;
+    }
+    asm volatile("" ::: "memory");  // the next block reuses the staging area after these reads
   }
 }
 

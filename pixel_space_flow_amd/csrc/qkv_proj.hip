@@ -155,18 +155,36 @@ __device__ __forceinline__ void proj_tile(
       }
     }
   }
-  if (!tvalid) continue;
-  uint16_t* orow = kind == 0 ? q_out + ((int64_t)t * Hq + gh) * 128
-                 : kind == 1 ? k_out + ((int64_t)t * Hkv + (gh - Hq)) * 128
-                             : v_out + ((int64_t)t * Hkv + (gh - Hq - Hkv)) * 128;
+  // The 32 x 128 block goes out through LDS, so that each lane stores whole 16-byte
+  // chunks and four lanes-of-16 cover four complete 256-byte rows.  The tile buffers are
+  // free: the main loop ends with a barrier after its last fragment read.  Wave w stages in
+  // 8 KB of its own 16 KB (row = token, chunk c of a row in slot c ^ (row mod 16)).
+  uint8_t* ob = ((wave >> 1) == 0 ? lw0 : (wave >> 1) == 1 ? lw1 : (wave >> 1) == 2 ? lx0 : lx1) +
+                (wave & 1) * 16384 + ti * 8192;
 #pragma unroll
   for (int fi = 0; fi < 4; ++fi)
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       const uint32_t lo = pack_bf16x2(acc_t[fi][rg * 4 + 0], acc_t[fi][rg * 4 + 1]);
       const uint32_t hi = pack_bf16x2(acc_t[fi][rg * 4 + 2], acc_t[fi][rg * 4 + 3]);
-      *reinterpret_cast<uint2*>(orow + fi * 32 + rg * 8 + 4 * hl) = make_uint2(lo, hi);
+      const int slot = (fi * 4 + rg) ^ (col & 15);
+      *reinterpret_cast<uint2*>(ob + col * 256 + slot * 16 + hl * 8) = make_uint2(lo, hi);
     }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the block is in LDS
+  asm volatile("" ::: "memory");
+  const int tb = t0 + tg * 32 * TW + ti * 32;  // first token of the block
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 4 * i + (lane >> 4), c = lane & 15;
+    const uint4 vrow = *reinterpret_cast<const uint4*>(ob + r * 256 + ((c ^ (r & 15)) * 16));
+    const int tr = tb + r;
+    if (tr < N) {
+      uint16_t* orow = kind == 0 ? q_out + ((int64_t)tr * Hq + gh) * 128
+                     : kind == 1 ? k_out + ((int64_t)tr * Hkv + (gh - Hq)) * 128
+                                 : v_out + ((int64_t)tr * Hkv + (gh - Hq - Hkv)) * 128;
+      *reinterpret_cast<uint4*>(orow + c * 8) = vrow;
+    }
+  }
   }
 }
 
