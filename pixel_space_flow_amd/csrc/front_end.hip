@@ -37,38 +37,47 @@ constexpr int kPatchK = 3 * kPatch * kPatch;  // 768
 constexpr int kStreamThreads = 256;
 constexpr int kSinDim = 256;
 
-int64_t stream_grid(int64_t items) {
-  int64_t blocks = (items + kStreamThreads - 1) / kStreamThreads;
-  const int64_t cap = 256 * 32;
-  return blocks < 1 ? 1 : (blocks > cap ? cap : blocks);
-}
-
 // ---- patchify --------------------------------------------------------------------------
-// One item = 16 pixels of one (image, channel, pixel row, patch column): 64 contiguous
-// bytes read (consecutive items are consecutive in memory) and 32 bytes written into the
-// patch's row at (channel, ky).
+// One strip = up to 16 consecutive patches of one patch row (image b, patch row py, patches
+// px0 .. px0 + 15).  Its pixels are 3 channels x 16 pixel rows of 16 * 16 contiguous floats:
+// 48 runs of up to 1 KB, read with consecutive lanes on consecutive 16-byte pieces.  They are
+// rounded to bf16 into a patch-major LDS image (row stride 776 elements, so that the
+// patches' rows fall on different banks) and leave as whole 1536-byte patch rows, again with
+// consecutive lanes on consecutive 16-byte pieces.
+constexpr int kStrip = 16;               // patches per strip
+constexpr int kStagedRow = kPatchK + 8;  // bf16 per staged patch row
 __global__ __launch_bounds__(kStreamThreads) void patchify_bf16_kernel(
-    const float* __restrict__ z, int64_t items, int H, int gw, int64_t P,
+    const float* __restrict__ z, int64_t strips, int H, int W, int gw, int spr, int64_t P,
     uint16_t* __restrict__ patches) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < items; i += stride) {
-    const int px = (int)(i % gw);
-    int64_t rest = i / gw;
-    const int y = (int)(rest % H);
-    rest /= H;
-    const int c = (int)(rest % 3);
-    const int64_t b = rest / 3;
-    const float4* src = reinterpret_cast<const float4*>(z + i * kPatch);
-    const float4 a0 = src[0], a1 = src[1], a2 = src[2], a3 = src[3];
-    const int py = y >> 4, ky = y & 15;
-    uint16_t* dst = patches + (b * P + (int64_t)py * gw + px) * kPatchK + c * 256 + ky * 16;
-    uint4 lo, hi;
-    lo.x = pack_bf16x2(a0.x, a0.y); lo.y = pack_bf16x2(a0.z, a0.w);
-    lo.z = pack_bf16x2(a1.x, a1.y); lo.w = pack_bf16x2(a1.z, a1.w);
-    hi.x = pack_bf16x2(a2.x, a2.y); hi.y = pack_bf16x2(a2.z, a2.w);
-    hi.z = pack_bf16x2(a3.x, a3.y); hi.w = pack_bf16x2(a3.z, a3.w);
-    reinterpret_cast<uint4*>(dst)[0] = lo;
-    reinterpret_cast<uint4*>(dst)[1] = hi;
+  __shared__ __attribute__((aligned(16))) uint16_t st[kStrip * kStagedRow];
+  const int gh = H / kPatch;
+  for (int64_t s = blockIdx.x; s < strips; s += gridDim.x) {
+    const int sx = (int)(s % spr);
+    const int64_t rest = s / spr;
+    const int py = (int)(rest % gh);
+    const int64_t b = rest / gh;
+    const int px0 = sx * kStrip;
+    const int np = gw - px0 < kStrip ? gw - px0 : kStrip;  // patches in this strip
+    const int ncols = np * kPatch;                         // pixels per run
+    for (int u = threadIdx.x; u < 3 * kPatch * 64; u += kStreamThreads) {
+      const int run = u >> 6, x = 4 * (u & 63);  // run = channel * 16 + ky
+      if (x < ncols) {
+        const int c = run >> 4, ky = run & 15;
+        const float4 a = *reinterpret_cast<const float4*>(
+            z + ((b * 3 + c) * H + (int64_t)(py * kPatch + ky)) * W + px0 * kPatch + x);
+        uint2 w;
+        w.x = pack_bf16x2(a.x, a.y);
+        w.y = pack_bf16x2(a.z, a.w);
+        *reinterpret_cast<uint2*>(st + (x >> 4) * kStagedRow + c * 256 + ky * 16 + (x & 15)) = w;
+      }
+    }
+    __syncthreads();
+    for (int u = threadIdx.x; u < np * (kPatchK / 8); u += kStreamThreads) {
+      const int p = u / (kPatchK / 8), e = (u - p * (kPatchK / 8)) * 8;
+      *reinterpret_cast<uint4*>(patches + (b * P + (int64_t)py * gw + px0 + p) * kPatchK + e) =
+          *reinterpret_cast<const uint4*>(st + p * kStagedRow + e);
+    }
+    __syncthreads();  // the next strip reuses the staging area
   }
 }
 
@@ -358,11 +367,13 @@ __global__ __launch_bounds__(kThreads, 1) void merge_gemm_kernel(
 hipError_t launch_gen_patchify(const float* z, int B, int H, int W, void* patches,
                                hipStream_t stream) {
   const int gw = W / kPatch;
-  const int64_t items = (int64_t)B * 3 * H * gw;
-  if (items == 0) return hipSuccess;
+  const int spr = (gw + kStrip - 1) / kStrip;  // strips per patch row
+  const int64_t strips = (int64_t)B * (H / kPatch) * spr;
+  if (strips == 0) return hipSuccess;
   const int64_t P = (int64_t)(H / kPatch) * gw;
-  hipLaunchKernelGGL(patchify_bf16_kernel, dim3((unsigned)stream_grid(items)),
-                     dim3(kStreamThreads), 0, stream, z, items, H, gw, P,
+  const int64_t cap = 256 * 8;
+  hipLaunchKernelGGL(patchify_bf16_kernel, dim3((unsigned)(strips < cap ? strips : cap)),
+                     dim3(kStreamThreads), 0, stream, z, strips, H, W, gw, spr, P,
                      static_cast<uint16_t*>(patches));
   return hipGetLastError();
 }
