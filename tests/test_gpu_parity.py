@@ -364,6 +364,32 @@ def test_attn_edges(neo, dtype, n_img, n_pre, Hq, Hkv):
     np.testing.assert_allclose(H.host(lse).T, lse_ref, atol=2e-3 if dtype == "bf16" else 1e-5)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_attn_many_samples_loose_bounds(neo, dtype):
+    """24 small samples (some with no queries, some with no prefix) and max_seqlen bounds well
+    above the true maxima.  The bounds only size the grid: the surplus workgroups find no rows
+    and every sample's rows still match the oracle."""
+    torch = _cuda()
+    rng = np.random.default_rng(2024)
+    n_img = [int(x) for x in rng.integers(0, 41, size=24)]
+    n_img[5] = 0
+    n_pre = [int(x) for x in rng.integers(0, 71, size=24)]
+    n_pre[3] = 0
+    n_pre[5] = 0
+    c = _random_case(rng, n_img, n_pre, 8, 2, dtype, wscale=0.5)
+    _say(f"attention 24 samples, loose bounds {max(n_img) + 50}/{max(n_pre) + 30} {dtype}")
+    d = dtype
+    out, lse = neo.gen_attn_fwd(H.dev(c["q"], d), H.dev(c["k"], d), H.dev(c["v"], d),
+                                H.dev(c["kp"], d), H.dev(c["vp"], d), H.dev_i32(c["cu_q"]),
+                                H.dev_i32(c["cu_p"]), max(n_img) + 50, max(n_pre) + 30,
+                                return_lse=True)
+    torch.cuda.synchronize()
+    ref, lse_ref = oracle.gen_attn(c["q"], c["k"], c["v"], c["kp"], c["vp"], c["cu_q"], c["cu_p"],
+                                   with_lse=True)
+    H.assert_close(H.host(out), ref, dtype, "attention, many samples")
+    np.testing.assert_allclose(H.host(lse).T, lse_ref, atol=2e-3 if dtype == "bf16" else 1e-5)
+
+
 def test_attn_peaky_softmax(neo):
     """Large-norm queries and keys make the softmax peaky (the lazy rescale path is
     exercised on later tiles and score errors are not averaged away)."""
