@@ -120,7 +120,8 @@ neo_status neo_qknorm_rope3(const void *q_in, const void *k_in, void *q_out, voi
  *     the host.  The kernels clamp every cu_seqlens entry into [0, Tq] and
  *     [0, Tp], so malformed offsets give wrong numbers, never a stray access.
  *   max_seqlen_q, max_seqlen_prefix: host-side upper bounds of the per-sample
- *     lengths (no device-to-host copy is made); they size the launch grid and
+ *     lengths (no device-to-host copy is made), at most total_q and total_prefix
+ *     (NEO_ERR_SHAPE otherwise); they size the launch grid and
  *     must not be below the true maxima (a precondition, as in varlen flash
  *     attention: rows and keys beyond the bound are not computed).  One
  *     sample's K or V rows must span less than 2 GiB (max_seqlen * Hkv * 256 B
@@ -206,7 +207,8 @@ neo_status neo_qkv_proj_norm_rope(const void *x, const void *w_qkv, int64_t N, i
  *                 it is broken the outputs are wrong, but every read stays
  *                 within the sample's rows.
  *   cu_seqlens    [B+1] int32, device: sample s is rows [cu[s], cu[s+1]).
- *   max_seqlen    host-side bound on the sample lengths; total = T.
+ *   max_seqlen    host-side bound on the sample lengths, at most T (NEO_ERR_SHAPE
+ *                 otherwise); total = T.
  *   softmax_scale <= 0 means 1/sqrt(128).
  *   out           [T, Hq, 128] bf16; lse optional [Hq, T] fp32 (natural log).
  *   dtype         NEO_BF16 only (the understanding branch is bf16, [A]

@@ -533,6 +533,17 @@ def test_prefill_run_beyond_probe(neo):
     _prefill_case(neo, d, "run beyond one probe", rows=rows)
 
 
+def test_prefill_loose_bound(neo):
+    """max_len at its largest allowed value, the total row count (311 against a longest
+    sample of 213), only sizes the grid: the surplus workgroups find no rows (under the
+    heaviest-first order they are the first to start), and every row still matches the
+    oracle."""
+    d = dict(W.prefill_layout(PREFILL_LAYOUTS["ragged"], 8, 2, seed=77))
+    assert int(d["max_len"]) < int(d["cu"][-1])
+    d["max_len"] = int(d["cu"][-1])
+    _prefill_case(neo, d, "loose max_len")
+
+
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (32, 4), (12, 4)])
 def test_prefill_heads(neo, hq, hkv):
     d = W.prefill_layout([[("text", 40), ("image", 70), ("text", 9)], [("text", 33)]], hq, hkv,
