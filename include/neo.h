@@ -98,9 +98,10 @@ neo_status neo_qknorm_rope3(const void *q_in, const void *k_in, void *q_out, voi
  * neo_gen_attn_fwd -- generation-pass attention of the image queries over
  * [frozen prefix ; image block], no mask, no cache write.
  *
- * Defined by [A] §Mixture of Transformers (the generation pass reads the keys
- * and values the understanding pass wrote, with update_cache=False) and
- * §GQA fusion does not apply (the generation pass is unmasked).  For sample b,
+ * Defined by [A] §Mixture of Transformers (the generation branch only reads
+ * the cache that the understanding branch filled; it is called with
+ * update_cache=False) and §GQA fusion does not apply (the generation graph
+ * takes no attention mask at all).  For sample b,
  * query row i in [cu_seqlens_q[b], cu_seqlens_q[b+1]) and query head h, with
  * g = h / (Hq / Hkv):
  *     keys    = k_prefix rows [cu_seqlens_prefix[b], cu_seqlens_prefix[b+1])
@@ -146,13 +147,15 @@ neo_status neo_gen_attn_fwd(const void *q, const void *k_img, const void *v_img,
  * pixel-space rectified flow, in place:
  *     v = (x0_pred - z) / max(1 - t, t_eps);   z <- z + (t_next - t) * v
  * ([A] §Flow matching without a VAE and §Runtime / metadata status; [B] §2.7).
- * patchify is a pure permutation, so the update is elementwise on any layout.
+ * Cutting the image into patches only reorders its elements, so the update is
+ * the same elementwise map on any layout.
  *
  *   z        [n] fp32, device: read and written.
  *   x0_pred  [n] fp32, device: read.  May not partially overlap z.
  *   n >= 0 (0 is a no-op).
- *   t, t_next finite with t <= t_next; t_eps > 0 and finite (0.02 is the
- *   value real inference uses, [A] §Dead or misleading upstream details).
+ *   t, t_next finite with t <= t_next; t_eps > 0 and finite (0.02: the example
+ *   scripts keep the function default and never read the config's 0.05, [A]
+ *   §Dead or misleading upstream details).
  *   Arithmetic is fp32: z + c*(x0_pred - z) with c = (t_next - t)/max(1-t, t_eps)
  *   formed once in double on the host.
  */
@@ -222,15 +225,19 @@ neo_status neo_prefill_attn_fwd(const void *q, const void *k, const void *v,
                                 void *out, float *lse, neo_dtype dtype, void *hip_stream);
 
 /*
- * neo_cfg_path -- which classifier-free guidance path a flow step takes
- * ([B] §2.7, the four code paths of the main loop).  Guidance is on when
- * cfg_interval_lo < t < cfg_interval_hi, or always when cfg_interval_lo == 0;
- * then, with exact comparisons as on the pages:
- *   1  guidance off, or cfg_scale == img_cfg_scale == 1: one forward (cond)
- *   2  img_cfg_scale == 1: cond and text-uncond (image context kept)
- *   3  cfg_scale == img_cfg_scale: cond and full uncond
- *   4  otherwise: all three branches
- * A caller uses it to decide which branch forwards to run.  Pure host function.
+ * neo_cfg_path -- which branch forwards a guided flow step needs ([B] §2.7,
+ * three-branch guidance).  Written per branch, the guided velocity is
+ *     w_c v_c + w_tu v_tu + w_u v_u,
+ *     w_c = cfg_scale, w_tu = img_cfg_scale - cfg_scale, w_u = 1 - img_cfg_scale,
+ * while guidance is active: for cfg_interval_lo < t < cfg_interval_hi, and for
+ * every t when cfg_interval_lo == 0.  Outside it the conditional velocity is
+ * used alone (w = 1, 0, 0).  The conditional forward always runs; each other
+ * branch runs when its weight is non-zero (scales compared exactly).  Returns
+ *   1  conditional only              (w_tu = w_u = 0)
+ *   2  plus text-uncond              (w_u = 0: img_cfg_scale == 1)
+ *   3  plus full uncond              (w_tu = 0: equal scales)
+ *   4  all three branches
+ * Pure host function.
  */
 int neo_cfg_path(float t, float cfg_scale, float img_cfg_scale, float cfg_interval_lo,
                  float cfg_interval_hi);
@@ -240,15 +247,12 @@ int neo_cfg_path(float t, float cfg_scale, float img_cfg_scale, float cfg_interv
  * predictions fused with the x0-to-velocity Euler step, in place, one pass
  * over the pixels ([B] §2.7: three-branch guidance; [A] §Flow matching without
  * a VAE and §Runtime / metadata status: each branch predicts x0 for the same z
- * from its own frozen prefix).  With v_b = (x0_b - z) / max(1 - t, t_eps):
- *   path 1: v = v_c
- *   path 2: v = v_tu + cfg_scale (v_c - v_tu)
- *   path 3: v = v_u  + cfg_scale (v_c - v_u)
- *   path 4: v = v_u  + cfg_scale (v_c - v_tu) + img_cfg_scale (v_tu - v_u)
- * and z <- z + (t_next - t) v, the path chosen as neo_cfg_path does.  The
- * weights of every path sum to one, so the library forms the guided x0 with
- * those weights and takes one Euler step: z + c*(sum_b w_b x0_b - z), c and the
- * weights computed once in double on the host, the pass in fp32.
+ * from its own frozen prefix).  With v_b = (x0_b - z) / max(1 - t, t_eps) and
+ * the weights w_b of neo_cfg_path,
+ *     v = sum_b w_b v_b   over the branches with a non-zero weight,
+ * and z <- z + (t_next - t) v.  The weights sum to one, so the library forms
+ * the guided x0 with them and takes one Euler step: z + c*(sum_b w_b x0_b - z),
+ * c and the weights computed once in double on the host, the pass in fp32.
  *
  *   z               [n] fp32, device: read and written.
  *   x0_cond         [n] fp32, device: the conditional branch; always read.

@@ -123,7 +123,7 @@ void oracle_norm_rope(const double *x, double *y, int64_t T, int64_t H,
 /*
  * Generation-pass attention, [A] §Mixture of Transformers (the generation pass
  * reads, and does not update, the frozen understanding-branch cache) and
- * §GQA fusion does not apply (the generation pass is unmasked).
+ * §GQA fusion does not apply (the generation graph takes no attention mask).
  *
  * For sample b, image query i (global row cu_q[b] + i) and query head h,
  * the key/value set is the prefix rows [cu_p[b], cu_p[b+1]) of k_pre/v_pre
@@ -208,41 +208,45 @@ void oracle_euler_step(double *z, const double *x0, int64_t n,
 }
 
 /*
- * Which guidance path a step takes, [B] §2.7 (the four code paths of the
- * three-branch guidance in the main loop).  Guidance is on when t lies strictly
- * inside the interval (lo, hi), or always when the interval starts at 0.
- *   1: guidance off, or gamma == gamma_img == 1   (one forward: cond)
- *   2: gamma_img == 1                             (cond and text-uncond)
- *   3: gamma == gamma_img                         (cond and full uncond)
- *   4: otherwise                                  (all three branches)
- * The comparisons are exact, as on the pages.
+ * Guidance weights, [B] §2.7 (three-branch guidance over the cond, text-uncond
+ * and full-uncond forwards).  Its full form
+ *     v = v_u + gamma (v_c - v_tu) + gamma_img (v_tu - v_u)
+ * is, collected per branch,
+ *     v = gamma v_c + (gamma_img - gamma) v_tu + (1 - gamma_img) v_u,
+ * and the page's cheaper code paths are exactly this sum with the branches of
+ * zero weight left out.  Guidance acts for t strictly inside (lo, hi), and for
+ * every t when lo is 0; otherwise the cond velocity is used alone.
+ */
+static void cfg_weights(double t, double gamma, double gamma_img, double lo, double hi,
+                        double w[3])
+{
+    int active = lo == 0.0 || (lo < t && t < hi);
+    w[0] = active ? gamma : 1.0;
+    w[1] = active ? gamma_img - gamma : 0.0;
+    w[2] = active ? 1.0 - gamma_img : 0.0;
+}
+
+/*
+ * Which forwards a step needs: the cond branch always, each other branch when
+ * its weight is non-zero.  1 = cond only, 2 = + text-uncond, 3 = + full uncond,
+ * 4 = all three.
  */
 int oracle_cfg_path(double t, double gamma, double gamma_img, double lo, double hi)
 {
-    int use_cfg = (t > lo && t < hi) || lo == 0.0;
-    if (!use_cfg || (gamma == 1.0 && gamma_img == 1.0))
-        return 1;
-    if (gamma_img == 1.0)
-        return 2;
-    if (gamma == gamma_img)
-        return 3;
-    return 4;
+    double w[3];
+    cfg_weights(t, gamma, gamma_img, lo, hi, w);
+    return 1 + (w[1] != 0.0) + 2 * (w[2] != 0.0);
 }
 
 /*
  * Classifier-free guidance over the conditioning branches, then one Euler step:
- * [B] §2.7 (three KV caches -- cond, text-uncond with the image context kept,
- * full uncond -- one forward each per step, combined by the three-branch
- * guidance formula) and [A] §Flow matching without a VAE (each branch's head
- * predicts x0, which the sampler turns into a velocity for the shared z).
- * Per element, in the pages' order: every needed branch's velocity
- * v_b = (x0_b - z) / max(1 - t, t_eps), then
- *   path 1: v = v_c
- *   path 2: v = v_tu + gamma (v_c - v_tu)
- *   path 3: v = v_u  + gamma (v_c - v_u)
- *   path 4: v = v_u  + gamma (v_c - v_tu) + gamma_img (v_tu - v_u)
- * and z <- z + (t_next - t) v.  Branch inputs the path does not read may be
- * NULL.
+ * [B] §2.7 (one forward per needed KV cache and step, combined by the
+ * three-branch guidance above) and [A] §Flow matching without a VAE (each
+ * branch's head predicts x0, which the sampler turns into a velocity for the
+ * shared z).  Per element: each needed branch's velocity
+ * v_b = (x0_b - z) / max(1 - t, t_eps), the guided velocity
+ * v = sum_b w_b v_b over the branches of non-zero weight, and
+ * z <- z + (t_next - t) v.  Branch inputs of zero weight may be NULL.
  */
 void oracle_euler_step_cfg(double *z, const double *x0_c, const double *x0_tu,
                            const double *x0_u, int64_t n, double t, double t_next,
@@ -250,24 +254,15 @@ void oracle_euler_step_cfg(double *z, const double *x0_c, const double *x0_tu,
                            double hi)
 {
     double denom = fmax(1.0 - t, t_eps);
-    int path = oracle_cfg_path(t, gamma, gamma_img, lo, hi);
+    double w[3];
+    cfg_weights(t, gamma, gamma_img, lo, hi, w);
+    const double *x0[3] = {x0_c, x0_tu, x0_u};
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
-        double v_c = (x0_c[i] - z[i]) / denom;
-        double v;
-        if (path == 1) {
-            v = v_c;
-        } else if (path == 2) {
-            double v_tu = (x0_tu[i] - z[i]) / denom;
-            v = v_tu + gamma * (v_c - v_tu);
-        } else if (path == 3) {
-            double v_u = (x0_u[i] - z[i]) / denom;
-            v = v_u + gamma * (v_c - v_u);
-        } else {
-            double v_tu = (x0_tu[i] - z[i]) / denom;
-            double v_u = (x0_u[i] - z[i]) / denom;
-            v = v_u + gamma * (v_c - v_tu) + gamma_img * (v_tu - v_u);
-        }
+        double v = w[0] * ((x0[0][i] - z[i]) / denom);
+        for (int br = 1; br < 3; ++br)
+            if (w[br] != 0.0)
+                v += w[br] * ((x0[br][i] - z[i]) / denom);
         z[i] = z[i] + (t_next - t) * v;
     }
 }

@@ -316,15 +316,37 @@ neo_status neo_prefill_attn_fwd(const void* q, const void* k, const void* v,
                   "neo_prefill_attn_fwd launch");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Weights of the three branches' velocities in the guided velocity.  The full three-branch
+// guidance of [B] §2.7, v_u + g (v_c - v_tu) + gi (v_tu - v_u), collects to
+//     g v_c + (gi - g) v_tu + (1 - gi) v_u,
+// and its other code paths are this sum with a vanishing weight dropped.  The weights
+// always sum to one.  Guidance acts only for t strictly between the interval's ends, except
+// that an interval starting at 0 keeps it on for the whole trajectory; elsewhere the
+// conditional branch alone drives the step.  The differences of two floats are exact in
+// double, so a weight is zero exactly when its two scales are equal.
+struct CfgWeights {
+  double c, tu, u;
+};
+
+CfgWeights cfg_weights(float t, float g, float gi, float lo, float hi) {
+  const bool on = lo == 0.0f || (lo < t && t < hi);
+  if (!on) return {1.0, 0.0, 0.0};
+  return {(double)g, (double)gi - (double)g, 1.0 - (double)gi};
+}
+
+}  // namespace
+
+extern "C" {
+
 int neo_cfg_path(float t, float cfg_scale, float img_cfg_scale, float cfg_interval_lo,
                  float cfg_interval_hi) {
-  // the pages' loop: guidance on strictly inside the interval, or always when the
-  // interval starts at 0; then the four cases by exact comparison of the scales
-  const bool use_cfg = (t > cfg_interval_lo && t < cfg_interval_hi) || cfg_interval_lo == 0.0f;
-  if (!use_cfg || (cfg_scale == 1.0f && img_cfg_scale == 1.0f)) return 1;
-  if (img_cfg_scale == 1.0f) return 2;
-  if (cfg_scale == img_cfg_scale) return 3;
-  return 4;
+  // a step runs the conditional forward, plus each other branch whose weight is non-zero
+  const CfgWeights w = cfg_weights(t, cfg_scale, img_cfg_scale, cfg_interval_lo, cfg_interval_hi);
+  return 1 + (w.tu != 0.0 ? 1 : 0) + (w.u != 0.0 ? 2 : 0);
 }
 
 neo_status neo_fm_euler_step_cfg(float* z, const float* x0_cond, const float* x0_text_uncond,
@@ -341,19 +363,20 @@ neo_status neo_fm_euler_step_cfg(float* z, const float* x0_cond, const float* x0
     return fail(NEO_ERR_VALUE, "%s: guidance scales and interval must be finite", fn);
   if (t_eps <= 0.0f) return fail(NEO_ERR_VALUE, "%s: t_eps must be > 0", fn);
   if (t_next < t) return fail(NEO_ERR_VALUE, "%s: t_next < t", fn);
-  const int path = neo_cfg_path(t, cfg_scale, img_cfg_scale, cfg_interval_lo, cfg_interval_hi);
+  const CfgWeights cw = cfg_weights(t, cfg_scale, img_cfg_scale, cfg_interval_lo, cfg_interval_hi);
+  const int path = 1 + (cw.tu != 0.0 ? 1 : 0) + (cw.u != 0.0 ? 2 : 0);
   if (n == 0) return ok();
-  // branch inputs and weights (they sum to one on every path)
-  const double g = cfg_scale, gi = img_cfg_scale;
+  // the conditional branch, then every branch with a non-zero weight
   const float* x[3] = {x0_cond, nullptr, nullptr};
-  double w[3] = {1.0, 0.0, 0.0};
+  double w[3] = {cw.c, 0.0, 0.0};
   int nb = 1;
-  if (path == 2) {
-    x[1] = x0_text_uncond; w[0] = g; w[1] = 1.0 - g; nb = 2;
-  } else if (path == 3) {
-    x[1] = x0_uncond; w[0] = g; w[1] = 1.0 - g; nb = 2;
-  } else if (path == 4) {
-    x[1] = x0_text_uncond; x[2] = x0_uncond; w[0] = g; w[1] = gi - g; w[2] = 1.0 - gi; nb = 3;
+  if (cw.tu != 0.0) {
+    x[nb] = x0_text_uncond;
+    w[nb++] = cw.tu;
+  }
+  if (cw.u != 0.0) {
+    x[nb] = x0_uncond;
+    w[nb++] = cw.u;
   }
   if (!z) return fail(NEO_ERR_NULL, "%s: z is NULL", fn);
   for (int b = 0; b < nb; ++b)

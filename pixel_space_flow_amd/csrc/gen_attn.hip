@@ -2,8 +2,8 @@
 // no cache write, grouped-query heads.
 //
 // "SenseNova-U1.5 (NEO-unify) architecture": §Mixture of Transformers (the generation
-// pass reads the keys/values the understanding pass wrote and does not update the
-// cache) and §GQA fusion does not apply (the generation pass is unmasked).  For query
+// branch reads the cache filled by the understanding branch and leaves it unchanged)
+// and §GQA fusion does not apply (the generation graph has no attention mask input).  For query
 // head h the KV head is h / (Hq / Hkv).  The frozen cache is token-major [S, H, D]
 // ("SenseNova-U1 ... NEO-unify Architecture" paper notes, §4.4 KV cache reuse); the
 // prefix and the image block are two separate segments read in place, no concatenation.

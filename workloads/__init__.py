@@ -6,13 +6,13 @@ no attention, no flow-matching update).  Both the fp64 oracle and the HIP
 library consume what it returns.
 
 Shapes follow the pages:
-  * one LLM token covers a 32x32 pixel tile (SenseNova-U1.5 (NEO-unify)
-    architecture, §Vision tower), so 512^2 -> 256, 1024^2 -> 1024 and
+  * each backbone token stands for a 32x32 block of pixels (SenseNova-U1.5
+    (NEO-unify) architecture, §Vision tower), so 512^2 -> 256, 1024^2 -> 1024 and
     2048^2 -> 4096 image tokens;
   * head_dim 128 split into a temporal [0:64), height [64:96) and width
-    [96:128) slice, each fed by its own row of a 3-row position index, and all
-    tokens of one image share one temporal index equal to the text length
-    (same page, §Three rotary axes);
+    [96:128) slice, each fed by its own row of a 3-row position index; every
+    token of an image carries the same temporal position, the number of text
+    tokens before it (same page, §Three rotary axes);
   * the generation pass reads a frozen understanding-branch K/V prefix
     (same page, §Mixture of Transformers), stored token-major [S, H, D]
     (SenseNova-U1 paper notes, §4.4 KV cache reuse).
