@@ -51,6 +51,7 @@ def _load():
             build(force=True)
         lib = ctypes.CDLL(_LIB)
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         lib.oracle_split_rmsnorm.argtypes = [_dp, _dp, ctypes.c_int64, _dp, _dp, ctypes.c_double]
         lib.oracle_rope3.argtypes = [_dp, ctypes.c_int64, ctypes.c_int64, _ip,
                                      ctypes.c_double, ctypes.c_double]
@@ -85,6 +86,11 @@ def _ptr(a, typ):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of the oracle's parallel loops from now on (for timing runs)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def split_rmsnorm(x, w_t, w_hw, eps=1e-6) -> np.ndarray:

@@ -42,6 +42,17 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Thread count for the parallel loops that follow (n >= 1); timing only. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /*
  * Split-half QK-RMSNorm, [A] §Three rotary axes (last paragraph): dims [0:64)
  * of every head row are normalised with the temporal-half weight (q_norm /

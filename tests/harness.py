@@ -72,7 +72,10 @@ def assert_front_end(got, ref, what: str = ""):
     _, rel = errors(got, ref)
     assert worst <= FRONT_END_REL, f"{what}: max |err|/(|ref|+rms) {worst:.3e} > {FRONT_END_REL:.2e}"
     assert rel <= 5e-3, f"{what}: rel-L2 {rel:.3e} > 5e-3"
-    print(f"[parity] {what}: max |err|/(|ref|+rms) {worst:.3e} rel-L2 {rel:.3e}", flush=True)
+    max_abs = float(np.max(err)) if ref.size else 0.0
+    print(f"[parity] {what}: max |err|/(|ref|+rms) {worst:.3e} rel-L2 {rel:.3e} "
+          f"max-abs {max_abs:.3e} (max |ref| {float(np.max(np.abs(ref))) if ref.size else 0.0:.3g}, "
+          f"rms {rms:.3g})", flush=True)
     return worst, rel
 
 

@@ -131,3 +131,51 @@ def test_algorithmic_work_of_the_benchmark_workload():
     assert pro == 4096 * (40 * 128 * 2 * 2 + 12) == pytest.approx(83.94e6, rel=1e-4)
     assert euler == 3 * 2048 * 2048 * 12 == pytest.approx(150.99e6, rel=1e-4)
     assert attn == (4096 * (32 + 8) * 2 + 512 * 8 * 2) * 128 * 2 == pytest.approx(85.98e6, rel=1e-4)
+
+
+def test_per_call_summary():
+    """Median, mean, minimum and 90th percentile of per-call durations, ms in, us out."""
+    bench = _bench()
+    st = bench.stats_us([0.3, 0.1, 0.2, 0.4, 1.0])
+    assert st["median"] == pytest.approx(300.0)
+    assert st["mean"] == pytest.approx(400.0)
+    assert st["min"] == pytest.approx(100.0)
+    assert st["calls"] == 5
+    assert 400.0 <= st["p90"] <= 1000.0
+
+
+def test_path_figures_from_durations():
+    """Rates of the step path from per-kernel durations: attention TFLOP/s and its share of
+    the 2.5 PFLOP/s peak, the bandwidth-bound kernels' GB/s, tokens/s of the step."""
+    bench = _bench()
+    import workloads as W
+    w = W.make("large", pixels=False)
+    w.pixel_shape = (1, 3, 2048, 2048)
+    flops, pro_bytes, euler_bytes, _ = bench.algorithmic(w)
+    k = {"gen_attn": {"median": 250.0}, "qknorm_rope3": {"median": 20.0},
+         "fm_euler_step": {"median": 30.0}}
+    f = bench.path_figures(w, k, "median")
+    assert f["attention_tflops"] == pytest.approx(flops / 250e-6 / 1e12)
+    assert f["attention_frac"] == pytest.approx(flops / 250e-6 / 2.5e15)
+    assert f["prologue_gbs"] == pytest.approx(pro_bytes / 20e-6 / 1e9)
+    assert f["image_tokens_per_s"] == pytest.approx(4096 / 300e-6)
+    assert 0.0 < f["step_frac"] < 1.0
+
+
+def test_cpu_baseline_protocol():
+    """The oracle's timing leg on the small workload: all-core and one-thread figures,
+    median of three runs, the attention time scaled from the sampled query tokens."""
+    bench = _bench()
+    import oracle
+    import workloads as W
+    from tests import harness as H
+    w = W.make("small")
+    kp, vp = H.frozen_prefix(w)
+    c = bench.cpu_baseline(w, kp, vp, 8, 2)
+    assert c["kind"] == "oracle" and c["unit"] == "image-tokens/s"
+    assert c["cores"] == (os.cpu_count() or 1) and c["one_thread"]["cores"] == 1
+    s = c["seconds"]
+    assert s["step"] == pytest.approx(s["prologue"] + s["attention_scaled"] + s["euler"])
+    assert c["value"] == pytest.approx(w.Tq / s["step"])
+    assert "8 of 256" in c["sample"]
+    assert oracle.num_threads() == (os.cpu_count() or 1)
