@@ -138,8 +138,9 @@ neo_status neo_gen_attn_fwd(const void* q, const void* k_img, const void* v_img,
     return fail(NEO_ERR_SHAPE, "neo_gen_attn_fwd: one sample's K/V rows exceed 2 GiB");
   if (!isfinite(softmax_scale))
     return fail(NEO_ERR_VALUE, "neo_gen_attn_fwd: softmax_scale must be finite");
-  // grid size: one workgroup per (sample, KV head, 8 chunks of 32 query rows), or per
-  // (sample, KV head, 128 query rows) for fp32 -- must fit a 32-bit grid
+  // grid size: one workgroup per (sample, KV head, 8 chunks of 32 query rows) -- per 4
+  // chunks when that launch would have at most 128 workgroups --, or per (sample, KV head,
+  // 128 query rows) for fp32; must fit a 32-bit grid
   {
     const int64_t G = Hq / Hkv;
     const int64_t per = dtype == NEO_BF16 ? ((int64_t)G * ((max_seqlen_q + 31) / 32) + 7) / 8

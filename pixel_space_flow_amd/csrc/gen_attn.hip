@@ -58,8 +58,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kThreads = kAttnBf16Threads;   // 8 waves, two per SIMD
-constexpr int kWaves = kThreads / 64;
 constexpr int kBN = 64;                      // keys per LDS tile (one barrier per tile)
 constexpr int kRow = kHeadDim * 2;          // one K or V row in LDS (no padding)
 constexpr int kTileBytes = kBN * kRow;       // 16 KB
@@ -154,7 +152,11 @@ __device__ __forceinline__ int run_end(const int32_t* ix, int start, int n, int 
 // of a workgroup cut at end() of its last query, and each lane masking keys past its own
 // end().  ("SenseNova-U1 ... NEO-unify Architecture" paper notes, §2.5, Fig. 6: image
 // query blocks extend the key range, text blocks stay causal.)
-template <bool kPrefill>
+//
+// kWaves is 8 (two waves per SIMD, 64 query tokens of one KV group per workgroup) or 4 (one
+// wave per SIMD, 32 tokens): the 4-wave form gives a launch twice as many workgroups, for
+// grids that would otherwise leave CUs idle.
+template <bool kPrefill, int kWaves>
 __device__ __forceinline__ void attn_bf16_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_img,
     const uint16_t* __restrict__ v_img, const uint16_t* __restrict__ k_pre,
@@ -195,6 +197,8 @@ __device__ __forceinline__ void attn_bf16_body(
   const int nchunks = G * ((N + 31) / 32);
   if (cg * kWaves >= nchunks) return;  // whole workgroup idle
 
+  constexpr int kThreads = kWaves * 64;
+  constexpr int kBlk = 16 / kWaves;  // 1 KB staging blocks per wave and tile
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, col = lane & 31;
   const int c = cg * kWaves + wave;
@@ -257,14 +261,14 @@ __device__ __forceinline__ void attn_bf16_body(
   S.ntiles[1] = (N + kBN - 1) / kBN;
   int ntiles = S.ntiles[0] + S.ntiles[1];  // the prefill recomputes it from kmax below
 
-  // staging: wave w fills 1 KB blocks 2w and 2w+1 of each tile (rows 4*blk .. +3); lane
-  // L of block blk lands in row 4*blk + L/16, slot L%16 and so fetches chunk
-  // (L%16) ^ swz(row) of that row
+  // staging: wave w fills 1 KB blocks kBlk*w .. kBlk*w + kBlk-1 of each tile (block blk
+  // holds rows 4*blk .. +3); lane L of block blk lands in row 4*blk + L/16, slot L%16 and
+  // so fetches chunk (L%16) ^ swz(row) of that row
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  int goff[2];
+  int goff[kBlk];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = 4 * (2 * wave + i) + (lane >> 4);
+  for (int i = 0; i < kBlk; ++i) {
+    const int row = 4 * (kBlk * wave + i) + (lane >> 4);
     goff[i] = row * (int)S.row_bytes + (((lane & 15) ^ swz(row)) << 4);
   }
 
@@ -314,18 +318,18 @@ __device__ __forceinline__ void attn_bf16_body(
     __amdgpu_buffer_rsrc_t rk, rv;
     tile_rsrc(S, t, rk, rv);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kBlk; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rk, (__attribute__((address_space(3))) void*)(kbuf(buf) + (2 * wave_u + i) * 1024),
+          rk, (__attribute__((address_space(3))) void*)(kbuf(buf) + (kBlk * wave_u + i) * 1024),
           16, goff[i], 0, 0, 0);
   };
   auto load_v = [&](int t, int buf) {
     __amdgpu_buffer_rsrc_t rk, rv;
     tile_rsrc(S, t, rk, rv);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kBlk; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (__attribute__((address_space(3))) void*)(vbuf(buf) + (2 * wave_u + i) * 1024),
+          rv, (__attribute__((address_space(3))) void*)(vbuf(buf) + (kBlk * wave_u + i) * 1024),
           16, goff[i], 0, 0, 0);
   };
   // fragment reads from K buffer kb / V buffer vb, sub-tile half h
@@ -559,24 +563,26 @@ __device__ __forceinline__ void attn_bf16_body(
   }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void gen_attn_bf16_kernel(
+template <int kWaves>
+__global__ __launch_bounds__(kWaves * 64, 1) void gen_attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_img,
     const uint16_t* __restrict__ v_img, const uint16_t* __restrict__ k_pre,
     const uint16_t* __restrict__ v_pre, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_p, int Hq, int Hkv, int n_cg, int max_q, int max_p,
     int64_t Tq, int64_t Tp, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse) {
-  attn_bf16_body<false>(q, k_img, v_img, k_pre, v_pre, cu_q, cu_p, nullptr, Hq, Hkv, n_cg, max_q,
-                        max_p, Tq, Tp, scale_log2, out, lse);
+  attn_bf16_body<false, kWaves>(q, k_img, v_img, k_pre, v_pre, cu_q, cu_p, nullptr, Hq, Hkv, n_cg,
+                                max_q, max_p, Tq, Tp, scale_log2, out, lse);
 }
 
-__global__ __launch_bounds__(kThreads, 1) void prefill_attn_bf16_kernel(
+template <int kWaves>
+__global__ __launch_bounds__(kWaves * 64, 1) void prefill_attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ tidx, int Hq, int Hkv, int n_cg, int max_len, int64_t T,
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  attn_bf16_body<true>(q, k, v, k, v, cu, cu, tidx, Hq, Hkv, n_cg, max_len, 0, T, T,
-                       scale_log2, out, lse);
+  attn_bf16_body<true, kWaves>(q, k, v, k, v, cu, cu, tidx, Hq, Hkv, n_cg, max_len, 0, T, T,
+                               scale_log2, out, lse);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -680,6 +686,18 @@ __global__ __launch_bounds__(kF32Threads) void gen_attn_f32_kernel(
 
 }  // namespace
 
+// Workgroups of 8 waves while the launch has more than kSmallGrid of them; at or below it
+// (at most half of the 256 CUs busy) workgroups of 4 waves, twice as many.
+#ifndef NEO_ATTN_SMALL_GRID
+#define NEO_ATTN_SMALL_GRID 128
+#endif
+constexpr int64_t kSmallGrid = NEO_ATTN_SMALL_GRID;
+
+// waves per workgroup for `chunks` 32-row query chunks per (sample, KV head)
+int attn_waves(int64_t chunks, int64_t per_chunk_groups) {
+  return ((chunks + 7) / 8) * per_chunk_groups <= kSmallGrid ? 4 : 8;
+}
+
 hipError_t launch_gen_attn_bf16(const void* q, const void* k_img, const void* v_img,
                                 const void* k_pre, const void* v_pre, const int32_t* cu_q,
                                 const int32_t* cu_p, int B, int Hq, int Hkv, int max_q,
@@ -688,10 +706,12 @@ hipError_t launch_gen_attn_bf16(const void* q, const void* k_img, const void* v_
   if (max_q == 0 || Tq == 0) return hipSuccess;
   const int G = Hq / Hkv;
   const int64_t chunks = (int64_t)G * ((max_q + 31) / 32);
-  const int64_t n_cg = (chunks + kWaves - 1) / kWaves;
+  const int waves = attn_waves(chunks, (int64_t)Hkv * B);
+  const int64_t n_cg = (chunks + waves - 1) / waves;
   const int64_t blocks = n_cg * Hkv * B;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634073599246810019);
-  hipLaunchKernelGGL(gen_attn_bf16_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+  auto kern = waves == 8 ? gen_attn_bf16_kernel<8> : gen_attn_bf16_kernel<4>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(waves * 64), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_img),
                      static_cast<const uint16_t*>(v_img), static_cast<const uint16_t*>(k_pre),
                      static_cast<const uint16_t*>(v_pre), cu_q, cu_p, Hq, Hkv, (int)n_cg,
@@ -706,10 +726,12 @@ hipError_t launch_prefill_attn_bf16(const void* q, const void* k, const void* v,
   if (max_len == 0 || T == 0) return hipSuccess;
   const int G = Hq / Hkv;
   const int64_t chunks = (int64_t)G * ((max_len + 31) / 32);
-  const int64_t n_cg = (chunks + kWaves - 1) / kWaves;
+  const int waves = attn_waves(chunks, (int64_t)Hkv * B);
+  const int64_t n_cg = (chunks + waves - 1) / waves;
   const int64_t blocks = n_cg * Hkv * B;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634073599246810019);
-  hipLaunchKernelGGL(prefill_attn_bf16_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+  auto kern = waves == 8 ? prefill_attn_bf16_kernel<8> : prefill_attn_bf16_kernel<4>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(waves * 64), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), cu, tidx, Hq, Hkv, (int)n_cg, max_len, T,
                      scale_log2, static_cast<uint16_t*>(out), lse);

@@ -353,6 +353,9 @@ def _random_case(rng, n_img, n_pre, Hq, Hkv, dtype, wscale=1.0):
     ([40], [200], 6, 2),          # G = 3
     ([96], [33], 16, 2),          # G = 8: 4 waves x 2 heads per chunk group
     ([257], [511], 32, 8),        # odd lengths on the production head shape
+    # a grid of more than 128 eight-wave workgroups (the launch above that size), with
+    # ragged, tiny and empty samples; the cases above run the four-wave launch
+    ([700, 3, 1000, 64, 0, 513], [100, 0, 37, 255, 12, 64], 32, 8),
 ])
 def test_attn_edges(neo, dtype, n_img, n_pre, Hq, Hkv):
     torch = _cuda()
