@@ -317,22 +317,31 @@ def step_fn(neo, w, sets, shared):
     return step
 
 
-def per_call(step, calls, then=None):
-    """Per-kernel durations of `calls` steps after the warm-up: each kernel of each step
-    between its own pair of events.  `then`, if given, is enqueued right behind the timed
-    steps, before the host reads the events, so the device does not pause in between.
-    Returns stats_us per kernel."""
+def per_call_enqueue(step, calls):
+    """Warm up, then enqueue `calls` steps with each kernel between its own pair of events.
+    Returns the events; nothing waits for them, so work enqueued next follows without a
+    pause on the device."""
     import torch
     warm_up(step)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(calls)]
     for i in range(calls):
         step(i, evs[i])
-    if then is not None:
-        then()
-    torch.cuda.synchronize()
+    return evs
+
+
+def per_call_stats(evs):
+    """stats_us per kernel from per_call_enqueue's events (after the stream has drained)."""
     return {"qknorm_rope3": stats_us([e[0].elapsed_time(e[1]) for e in evs]),
             "gen_attn": stats_us([e[1].elapsed_time(e[2]) for e in evs]),
             "fm_euler_step": stats_us([e[2].elapsed_time(e[3]) for e in evs])}
+
+
+def per_call(step, calls):
+    """Per-kernel durations of `calls` steps after the warm-up (stats_us per kernel)."""
+    import torch
+    evs = per_call_enqueue(step, calls)
+    torch.cuda.synchronize()
+    return per_call_stats(evs)
 
 
 def path_figures(w, k_us, stat):
@@ -394,20 +403,14 @@ def main():
 
     # per-call durations: warm-up (at least WARM_MS of steps), then `calls` steps with every
     # kernel between its own events; the roofline and the per-kernel rates come from these.
-    # The W warm-up steps of the benchmark proper are enqueued right behind them, so the
-    # timed steps start on a settled device.
+    # The W warm-up steps of the benchmark proper are enqueued right behind them and the
+    # events are read only after the timed steps, so the device runs without a pause from
+    # the warm-up to the end of the timed steps (a pause of a few ms restarts the clock
+    # transient described at WARM_MS).
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
-
-    def bench_warmup():
-        for i in range(a.warmup):
-            step(i)
-    kus = None
-    if a.calls > 0:
-        kus = per_call(step, a.calls, then=bench_warmup)
-        print(f"[bench] per-call timing: {a.calls} steps after a {WARM_MS:g} ms warm-up; "
-              f"attention median {kus['gen_attn']['median']:.1f} us", file=sys.stderr, flush=True)
-    else:
-        bench_warmup()
+    pc_events = per_call_enqueue(step, a.calls) if a.calls > 0 else None
+    for i in range(a.warmup):
+        step(i)
 
     # the benchmark proper: W untimed steps (above), then exactly K steps between two
     # synchronisations
@@ -423,8 +426,10 @@ def main():
                 "fm_euler_step": stats_us([e[2].elapsed_time(e[3]) for e in events])}
     print(f"[bench] warm-up ({a.warmup} steps) and {a.steps} timed steps: {ms_step:.4f} ms/step",
           file=sys.stderr, flush=True)
-    if kus is None:
-        kus = steps_us
+    kus = per_call_stats(pc_events) if pc_events is not None else steps_us
+    if pc_events is not None:
+        print(f"[bench] per-call timing: {a.calls} steps after a {WARM_MS:g} ms warm-up; "
+              f"attention median {kus['gen_attn']['median']:.1f} us", file=sys.stderr, flush=True)
 
     attn_mean_s = kus["gen_attn"]["mean"] * 1e-6
     achieved = flops / attn_mean_s / 1e12

@@ -563,27 +563,32 @@ __device__ __forceinline__ void attn_bf16_body(
   }
 }
 
-template <int kWaves>
-__global__ __launch_bounds__(kWaves * 64, 1) void gen_attn_bf16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_img,
-    const uint16_t* __restrict__ v_img, const uint16_t* __restrict__ k_pre,
-    const uint16_t* __restrict__ v_pre, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ cu_p, int Hq, int Hkv, int n_cg, int max_q, int max_p,
-    int64_t Tq, int64_t Tp, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse) {
-  attn_bf16_body<false, kWaves>(q, k_img, v_img, k_pre, v_pre, cu_q, cu_p, nullptr, Hq, Hkv, n_cg,
-                                max_q, max_p, Tq, Tp, scale_log2, out, lse);
-}
+// The eight- and four-wave launches are separate kernels (distinct names in kernel traces).
+#define NEO_GEN_ATTN_KERNEL(name, waves)                                                       \
+  __global__ __launch_bounds__(waves * 64, 1) void name(                                       \
+      const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_img,                      \
+      const uint16_t* __restrict__ v_img, const uint16_t* __restrict__ k_pre,                  \
+      const uint16_t* __restrict__ v_pre, const int32_t* __restrict__ cu_q,                    \
+      const int32_t* __restrict__ cu_p, int Hq, int Hkv, int n_cg, int max_q, int max_p,       \
+      int64_t Tq, int64_t Tp, float scale_log2, uint16_t* __restrict__ out,                    \
+      float* __restrict__ lse) {                                                               \
+    attn_bf16_body<false, waves>(q, k_img, v_img, k_pre, v_pre, cu_q, cu_p, nullptr, Hq, Hkv,  \
+                                 n_cg, max_q, max_p, Tq, Tp, scale_log2, out, lse);            \
+  }
+NEO_GEN_ATTN_KERNEL(gen_attn_bf16_kernel, 8)
+NEO_GEN_ATTN_KERNEL(gen_attn_bf16_w4_kernel, 4)
 
-template <int kWaves>
-__global__ __launch_bounds__(kWaves * 64, 1) void prefill_attn_bf16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ tidx, int Hq, int Hkv, int n_cg, int max_len, int64_t T,
-    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  attn_bf16_body<true, kWaves>(q, k, v, k, v, cu, cu, tidx, Hq, Hkv, n_cg, max_len, 0, T, T,
-                               scale_log2, out, lse);
-}
+#define NEO_PREFILL_ATTN_KERNEL(name, waves)                                                   \
+  __global__ __launch_bounds__(waves * 64, 1) void name(                                       \
+      const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,                          \
+      const uint16_t* __restrict__ v, const int32_t* __restrict__ cu,                          \
+      const int32_t* __restrict__ tidx, int Hq, int Hkv, int n_cg, int max_len, int64_t T,     \
+      float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {                 \
+    attn_bf16_body<true, waves>(q, k, v, k, v, cu, cu, tidx, Hq, Hkv, n_cg, max_len, 0, T, T,  \
+                                scale_log2, out, lse);                                         \
+  }
+NEO_PREFILL_ATTN_KERNEL(prefill_attn_bf16_kernel, 8)
+NEO_PREFILL_ATTN_KERNEL(prefill_attn_bf16_w4_kernel, 4)
 
 // ---------------------------------------------------------------------------------------
 // fp32 path
@@ -710,7 +715,7 @@ hipError_t launch_gen_attn_bf16(const void* q, const void* k_img, const void* v_
   const int64_t n_cg = (chunks + waves - 1) / waves;
   const int64_t blocks = n_cg * Hkv * B;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634073599246810019);
-  auto kern = waves == 8 ? gen_attn_bf16_kernel<8> : gen_attn_bf16_kernel<4>;
+  auto kern = waves == 8 ? gen_attn_bf16_kernel : gen_attn_bf16_w4_kernel;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(waves * 64), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_img),
                      static_cast<const uint16_t*>(v_img), static_cast<const uint16_t*>(k_pre),
@@ -730,7 +735,7 @@ hipError_t launch_prefill_attn_bf16(const void* q, const void* k, const void* v,
   const int64_t n_cg = (chunks + waves - 1) / waves;
   const int64_t blocks = n_cg * Hkv * B;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634073599246810019);
-  auto kern = waves == 8 ? prefill_attn_bf16_kernel<8> : prefill_attn_bf16_kernel<4>;
+  auto kern = waves == 8 ? prefill_attn_bf16_kernel : prefill_attn_bf16_w4_kernel;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(waves * 64), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), cu, tidx, Hq, Hkv, (int)n_cg, max_len, T,
