@@ -154,8 +154,8 @@ __device__ __forceinline__ int run_end(const int32_t* ix, int start, int n, int 
 // query blocks extend the key range, text blocks stay causal.)
 //
 // kWaves is 8 (two waves per SIMD, 64 query tokens of one KV group per workgroup) or 4 (one
-// wave per SIMD, 32 tokens): the 4-wave form gives a launch twice as many workgroups, for
-// grids that would otherwise leave CUs idle.
+// wave per SIMD, 32 tokens; the prefill's form for grids that would otherwise leave CUs
+// idle; the generation pass uses the split-key form below for those).
 template <bool kPrefill, int kWaves>
 __device__ __forceinline__ void attn_bf16_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_img,
@@ -563,6 +563,376 @@ __device__ __forceinline__ void attn_bf16_body(
   }
 }
 
+// Split-key form, for launches that would leave CUs idle (one or few short images).  A
+// workgroup of 8 waves covers 32 query tokens of one KV group (4 chunks of 32 query rows,
+// one per query head) and splits the keys between two groups of waves: waves 0-3 take
+// the first half, waves 4-7 the second, so every SIMD still runs two waves.  Keys are
+// counted in 32-key sub-tiles, each inside one segment (prefix first, then image): ns of
+// them; half 0 takes sub-tiles [0, ns0), half 1 [ns0, ns), ns0 = ceil(ns / 2).  LDS tile T
+// (64 rows, swizzled as above) holds half 0's sub-tile T in rows 0-31 and half 1's
+// sub-tile ns0 + T in rows 32-63, so each wave reads only its half of every tile and the
+// pipeline advances one 32-key step per tile: the step at sub-tile T issues the scores of
+// T + 1, the PV product of T - 1 and the weights of T.  Tile t lives in buffer t % 3; in
+// iteration T the waves read K tiles T + 1, T + 2 and V tiles T - 1, T, while K tile T + 3
+// and V tile T + 1 are loaded into the buffers of K tile T and V tile T - 2.  At the end the
+// second group hands its (m, l, O) to the first through LDS and the first group merges,
+// normalises and stores.  A half with no keys (ns = 1) contributes l = 0.
+__device__ __forceinline__ void gen_attn_split_body(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_img,
+    const uint16_t* __restrict__ v_img, const uint16_t* __restrict__ k_pre,
+    const uint16_t* __restrict__ v_pre, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_p, int Hq, int Hkv, int n_cg, int max_q, int max_p,
+    int64_t Tq, int64_t Tp, float scale_log2, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lk0[kTileBytes], lk1[kTileBytes],
+      lk2[kTileBytes], lv0[kTileBytes], lv1[kTileBytes], lv2[kTileBytes];
+  auto kbuf = [&](int b) __attribute__((always_inline)) -> uint8_t* {
+    return b == 0 ? lk0 : (b == 1 ? lk1 : lk2);
+  };
+  auto vbuf = [&](int b) __attribute__((always_inline)) -> uint8_t* {
+    return b == 0 ? lv0 : (b == 1 ? lv1 : lv2);
+  };
+  constexpr int kQW = 4;  // query waves per workgroup (one per key half pair)
+
+  const uint32_t id = xcd_remap(blockIdx.x, gridDim.x);
+  const int cg = (int)(id % (uint32_t)n_cg);
+  const int rest = (int)(id / (uint32_t)n_cg);
+  const int g = rest % Hkv;
+  const int b = rest / Hkv;
+
+  int64_t qa = cu_q[b], qb = cu_q[b + 1];
+  qa = qa < 0 ? 0 : (qa > Tq ? Tq : qa);
+  qb = qb < qa ? qa : (qb > Tq ? Tq : qb);
+  int64_t pa = cu_p[b], pb_ = cu_p[b + 1];
+  pa = pa < 0 ? 0 : (pa > Tp ? Tp : pa);
+  pb_ = pb_ < pa ? pa : (pb_ > Tp ? Tp : pb_);
+  const int N = (int)((qb - qa) < max_q ? (qb - qa) : max_q);
+  const int P = (int)((pb_ - pa) < max_p ? (pb_ - pa) : max_p);
+
+  const int G = Hq / Hkv;
+  const int nchunks = G * ((N + 31) / 32);
+  if (cg * kQW >= nchunks) return;  // whole workgroup idle
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, col = lane & 31;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int qw = wave & 3, hw = wave >> 2;  // query wave, key half
+  const int c = cg * kQW + qw;
+  const bool active = c < nchunks;
+  const int h = g * G + (active ? c % G : 0);
+  const int qi = (active ? c / G : 0) * 32 + col;
+  const bool qvalid = active && qi < N;
+
+  // 32-key sub-tiles: np0 in the prefix, then the image's
+  const int np0 = (P + 31) / 32, ns = np0 + (N + 31) / 32, ns0 = (ns + 1) / 2;
+  const int first = __builtin_amdgcn_readfirstlane(hw ? ns0 : 0);
+  const int count = __builtin_amdgcn_readfirstlane(hw ? ns - ns0 : ns0);
+  const bool work = active && count > 0;
+
+  const uint32_t row_bytes = (uint32_t)Hkv * kHeadDim * 2;
+  const uint8_t* kb0 = reinterpret_cast<const uint8_t*>(k_pre + (pa * Hkv + g) * kHeadDim);
+  const uint8_t* vb0 = reinterpret_cast<const uint8_t*>(v_pre + (pa * Hkv + g) * kHeadDim);
+  const uint8_t* kb1 = reinterpret_cast<const uint8_t*>(k_img + (qa * Hkv + g) * kHeadDim);
+  const uint8_t* vb1 = reinterpret_cast<const uint8_t*>(v_img + (qa * Hkv + g) * kHeadDim);
+  // keys of this half's sub-tile t that exist (0 past the half's end)
+  auto sub_rows = [&](int t) -> int {
+    const int gs = first + t;
+    const bool pre = gs < np0;
+    const int rows = (pre ? P : N) - 32 * (pre ? gs : gs - np0);
+    return t < count ? (rows < 32 ? rows : 32) : 0;
+  };
+  // buffer resources of this half's sub-tile t: from its first row to the end of its rows
+  auto sub_rsrc = [&](int t, bool isv) -> __amdgpu_buffer_rsrc_t {
+    const int gs = first + t;
+    const bool pre = gs < np0;
+    const int rows = sub_rows(t);
+    const uint32_t off = (uint32_t)(pre ? gs : gs - np0) * 32u * row_bytes;
+    const uint8_t* base = isv ? (pre ? vb0 : vb1) : (pre ? kb0 : kb1);
+    const uint32_t nbytes = rows <= 0 ? 0u : (uint32_t)rows * row_bytes;
+    return make_rsrc(base + (t < count ? off : 0u), nbytes);
+  };
+
+  // staging: wave w fills LDS rows 8w .. 8w+7 of each tile (blocks 2w, 2w+1), i.e. rows
+  // 8*qw .. 8*qw+7 of its own half's sub-tile
+  int goff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rin = 8 * qw + 4 * i + (lane >> 4);  // row inside the sub-tile (= LDS row % 32)
+    goff[i] = rin * (int)row_bytes + (((lane & 15) ^ swz(rin)) << 4);
+  }
+  // fragment offsets include the half's 32-row offset
+  int kofs[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st)
+    kofs[st] = (32 * hw + col) * kRow + (((2 * st + hl) ^ swz(col)) << 4);
+  const int j16 = lane & 15, grp = (lane >> 4) & 1;
+  int vofs[2][4];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int row = 8 * r + 4 * hl + (j16 >> 2);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int chunk = 4 * db + 2 * grp + ((j16 & 3) >> 1);
+      vofs[r][db] = (32 * hw + row) * kRow + ((chunk ^ swz(row)) << 4) + ((j16 & 1) << 3);
+    }
+  }
+
+  bf16x8 qf[8];
+  if (qvalid) {
+    const uint16_t* qr = q + ((qa + qi) * Hq + h) * kHeadDim + 8 * hl;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 16 * s));
+  } else {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(make_uint4(0, 0, 0, 0));
+  }
+
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+  float m = -INFINITY, lsum = 0.0f;
+
+  auto load_k = [&](int t, int buf) {
+    const __amdgpu_buffer_rsrc_t rk = sub_rsrc(t, false);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (__attribute__((address_space(3))) void*)(kbuf(buf) + (2 * wave_u + i) * 1024), 16,
+          goff[i], 0, 0, 0);
+  };
+  auto load_v = [&](int t, int buf) {
+    const __amdgpu_buffer_rsrc_t rv = sub_rsrc(t, true);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (__attribute__((address_space(3))) void*)(vbuf(buf) + (2 * wave_u + i) * 1024), 16,
+          goff[i], 0, 0, 0);
+  };
+  auto kread = [&](int kb, int st) -> bf16x8 {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(kbuf(kb) + kofs[st]));
+  };
+  auto vread = [&](const uint8_t* vb, int u, int db) -> bf16x8 {
+    const uint8_t* p = vb + 16 * u * kRow;
+    const uint2 lo = __builtin_bit_cast(
+        uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + vofs[0][db])));
+    const uint2 hi = __builtin_bit_cast(
+        uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + vofs[1][db])));
+    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+  };
+  // keys of sub-tile t past its rows score -inf
+  auto mask = [&](int t, f32x16& sacc) {
+    const int nvalid = sub_rows(t);
+    if (nvalid < 32) {
+      const int lim = nvalid - hl * 4;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if ((r >> 2) * 8 + (r & 3) >= lim) sacc[r] = -INFINITY;
+    }
+  };
+  auto exp_pair = [&](const f32x16& sacc, int i, uint32_t (&pk)[2][4], float& tsum) {
+    const int u = i >> 2, e = (i & 3) * 2;
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[u * 8 + e], scale_log2, -m));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[u * 8 + e + 1], scale_log2, -m));
+    pk[u][i & 3] = pack_bf16x2(p0, p1);
+    tsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[u][i & 3]), kOnes2, tsum,
+                                           false);
+  };
+  auto pack_p = [&](const uint32_t (&pk)[2][4], bf16x8 (&pw)[2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) pw[u] = as_bf16x8(make_uint4(pk[u][0], pk[u][1], pk[u][2], pk[u][3]));
+  };
+  bf16x8 kf[4], vf[4];
+  auto fetch = [&](int kb, int vb, int i, int r) __attribute__((always_inline)) {
+    kf[r] = kread(kb, i);
+    vf[r] = vread(vbuf(vb), i >> 2, i & 3);
+  };
+  // the same lazy-maximum step end as the unsplit body
+  auto finish_step = [&](int t, f32x16& scur, f32x16& snext, bf16x8 (&pcur)[2],
+                         uint32_t (&pk)[2][4], float tsum) {
+    pack_p(pk, pcur);
+    if (__ballot(!(tsum <= kTwoTau)) != 0) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m, mx * scale_log2);
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      m = mnew;
+      tsum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) exp_pair(scur, i, pk, tsum);
+      pack_p(pk, pcur);
+    }
+    lsum += tsum;
+    mask(t + 1, snext);
+  };
+
+  // prologue: K tiles 0, 1, 2 and V tile 0; V buffer 2 cleared (the PV product of the
+  // first step reads it against an all-zero P); scores of sub-tile 0
+  load_k(0, 0);
+  load_v(0, 0);
+  if (ns0 > 1) load_k(1, 1);
+  if (ns0 > 2) load_k(2, 2);
+  for (int i = tid; i < kTileBytes / 16; i += 512)
+    reinterpret_cast<uint4*>(lv2)[i] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+  const f32x16 zero16 = {};
+  f32x16 sa, sb;
+  bf16x8 pa_[2], pb2[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) pb2[u] = as_bf16x8(make_uint4(0, 0, 0, 0));
+  if (work) {
+    sa = zero16;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(0, i), qf[i], sa, 0, 0, 0);
+    mask(0, sa);
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) fetch(1, 2, k, k);
+  }
+
+  // iteration T (T6 = T % 6 compile-time): buffers T % 3, register roles by T % 2
+  auto iteration = [&](int T, auto t6) __attribute__((always_inline)) {
+    constexpr int T6 = decltype(t6)::value;
+    constexpr int b0 = T6 % 3, b1 = (T6 + 1) % 3, b2 = (T6 + 2) % 3;  // tiles T, T+1, T+2 (T-1)
+    f32x16& scur = (T6 & 1) == 0 ? sa : sb;
+    f32x16& snext = (T6 & 1) == 0 ? sb : sa;
+    bf16x8 (&pcur)[2] = (T6 & 1) == 0 ? pa_ : pb2;
+    bf16x8 (&pprev)[2] = (T6 & 1) == 0 ? pb2 : pa_;
+    const bool kmore = T + 3 < ns0, vmore = T + 1 < ns0;
+    if (!work) {
+      if (kmore) load_k(T + 3, b0);
+      if (vmore) load_v(T + 1, b1);
+    } else {
+      uint32_t pk[2][4];
+      float tsum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        {
+          const int ii = i + kPrefetch;
+          if (ii < 8)  // this step: K of sub-tile T+1, V of T-1 (buffer of tile T+2 mod 3)
+            fetch(b1, b2, ii, ii & 3);
+          else  // the first slots of the next step: K of T+2, V of T
+            fetch(b2, b0, ii - 8, ii & 3);
+        }
+        snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i & 3], qf[i], i == 0 ? zero16 : snext,
+                                                        0, 0, 0);
+        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 3], pprev[i >> 2], o[i & 3], 0, 0, 0);
+        if (i == kLoadSlotK && kmore) load_k(T + 3, b0);
+        if (i == kLoadSlotV && vmore) load_v(T + 1, b1);
+        __builtin_amdgcn_s_setprio(1);
+        exp_pair(scur, i, pk, tsum);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i == 7) finish_step(T, scur, snext, pcur, pk, tsum);
+      }
+    }
+    __syncthreads();
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C3 = std::integral_constant<int, 3>;
+  using C4 = std::integral_constant<int, 4>;
+  using C5 = std::integral_constant<int, 5>;
+  for (int T = 0; T < ns0; T += 6) {
+    iteration(T, C0{});
+    if (T + 1 >= ns0) break;
+    iteration(T + 1, C1{});
+    if (T + 2 >= ns0) break;
+    iteration(T + 2, C2{});
+    if (T + 3 >= ns0) break;
+    iteration(T + 3, C3{});
+    if (T + 4 >= ns0) break;
+    iteration(T + 4, C4{});
+    if (T + 5 >= ns0) break;
+    iteration(T + 5, C5{});
+  }
+  // PV product of the last sub-tile, ns0 - 1: V tile ns0 - 1 (buffer (ns0 - 1) % 3), its
+  // weights in pa_ (ns0 odd) or pb2 (ns0 even)
+  if (work) {
+    const uint8_t* va = vbuf((ns0 - 1) % 3);
+    bf16x8 pl[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) pl[u] = (ns0 & 1) ? pa_[u] : pb2[u];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(va, i >> 2, i & 3), pl[i >> 2],
+                                                         o[i & 3], 0, 0, 0);
+  }
+  float ltot = lsum + __shfl_xor(lsum, 32);
+  if (!work) ltot = 0.0f;
+
+  // merge: the second group's (m, l, O) through LDS (the K buffers and V buffer 0 hold the
+  // four waves' O, 16 KB each, V buffer 1 their m and l), combined by the first group
+  __syncthreads();
+  uint8_t* mo = qw == 0 ? lk0 : (qw == 1 ? lk1 : (qw == 2 ? lk2 : lv0));
+  float2* ml = reinterpret_cast<float2*>(lv1) + qw * 64 + lane;
+  if (hw == 1 && active) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg)
+        reinterpret_cast<float4*>(mo)[(db * 4 + rg) * 64 + lane] =
+            make_float4(o[db][rg * 4], o[db][rg * 4 + 1], o[db][rg * 4 + 2], o[db][rg * 4 + 3]);
+    *ml = make_float2(work ? m : -INFINITY, ltot);
+  }
+  __syncthreads();
+  if (hw == 0 && active) {
+    const float2 mlb = *ml;
+    const float mnew = fmaxf(m, mlb.x);
+    const float sa_ = __builtin_amdgcn_exp2f(m - mnew);
+    const float sb_ = mlb.y > 0.0f ? __builtin_amdgcn_exp2f(mlb.x - mnew) : 0.0f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const float4 ob = reinterpret_cast<const float4*>(mo)[(db * 4 + rg) * 64 + lane];
+        o[db][rg * 4] = o[db][rg * 4] * sa_ + ob.x * sb_;
+        o[db][rg * 4 + 1] = o[db][rg * 4 + 1] * sa_ + ob.y * sb_;
+        o[db][rg * 4 + 2] = o[db][rg * 4 + 2] * sa_ + ob.z * sb_;
+        o[db][rg * 4 + 3] = o[db][rg * 4 + 3] * sa_ + ob.w * sb_;
+      }
+    ltot = ltot * sa_ + mlb.y * sb_;
+    m = mnew;
+  }
+  __syncthreads();
+
+  // the first group normalises and stores, through LDS as in the unsplit body
+  uint8_t* ob = ((qw >> 1) == 0 ? lk0 : lk1) + (qw & 1) * 8192;
+  if (hw == 0 && active) {
+    const float inv = qvalid ? 1.0f / ltot : 0.0f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const uint32_t w0 = pack_bf16x2(o[db][rg * 4 + 0] * inv, o[db][rg * 4 + 1] * inv);
+        const uint32_t w1 = pack_bf16x2(o[db][rg * 4 + 2] * inv, o[db][rg * 4 + 3] * inv);
+        const int slot = (db * 4 + rg) ^ (col & 15);
+        *reinterpret_cast<uint2*>(ob + col * 256 + slot * 16 + hl * 8) = make_uint2(w0, w1);
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's rows are in LDS
+    asm volatile("" ::: "memory");
+    const int q0 = qi - col;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4), cch = lane & 15;
+      const uint4 vrow = *reinterpret_cast<const uint4*>(ob + r * 256 + ((cch ^ (r & 15)) * 16));
+      if (q0 + r < N)
+        *reinterpret_cast<uint4*>(out + ((qa + q0 + r) * Hq + h) * kHeadDim + cch * 8) = vrow;
+    }
+    if (qvalid && lse != nullptr && hl == 0)
+      lse[(int64_t)h * Tq + qa + qi] = (m + __log2f(ltot)) * 0.69314718055994530942f;
+  }
+}
+
 // The eight- and four-wave launches are separate kernels (distinct names in kernel traces).
 #define NEO_GEN_ATTN_KERNEL(name, waves)                                                       \
   __global__ __launch_bounds__(waves * 64, 1) void name(                                       \
@@ -576,7 +946,17 @@ __device__ __forceinline__ void attn_bf16_body(
                                  n_cg, max_q, max_p, Tq, Tp, scale_log2, out, lse);            \
   }
 NEO_GEN_ATTN_KERNEL(gen_attn_bf16_kernel, 8)
-NEO_GEN_ATTN_KERNEL(gen_attn_bf16_w4_kernel, 4)
+
+__global__ __launch_bounds__(512, 1) void gen_attn_bf16_split_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_img,
+    const uint16_t* __restrict__ v_img, const uint16_t* __restrict__ k_pre,
+    const uint16_t* __restrict__ v_pre, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_p, int Hq, int Hkv, int n_cg, int max_q, int max_p,
+    int64_t Tq, int64_t Tp, float scale_log2, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
+  gen_attn_split_body(q, k_img, v_img, k_pre, v_pre, cu_q, cu_p, Hq, Hkv, n_cg, max_q, max_p, Tq,
+                      Tp, scale_log2, out, lse);
+}
 
 #define NEO_PREFILL_ATTN_KERNEL(name, waves)                                                   \
   __global__ __launch_bounds__(waves * 64, 1) void name(                                       \
@@ -691,8 +1071,10 @@ __global__ __launch_bounds__(kF32Threads) void gen_attn_f32_kernel(
 
 }  // namespace
 
-// Workgroups of 8 waves while the launch has more than kSmallGrid of them; at or below it
-// (at most half of the 256 CUs busy) workgroups of 4 waves, twice as many.
+// Workgroups of 64 query tokens (8 waves) while the launch has more than kSmallGrid of them;
+// at or below it (at most half of the 256 CUs busy) workgroups of 32 query tokens, twice as
+// many: the generation pass splits their keys between two groups of 4 waves (the split-key
+// kernel), the prefill runs them as 4 waves.
 #ifndef NEO_ATTN_SMALL_GRID
 #define NEO_ATTN_SMALL_GRID 128
 #endif
@@ -711,12 +1093,14 @@ hipError_t launch_gen_attn_bf16(const void* q, const void* k_img, const void* v_
   if (max_q == 0 || Tq == 0) return hipSuccess;
   const int G = Hq / Hkv;
   const int64_t chunks = (int64_t)G * ((max_q + 31) / 32);
-  const int waves = attn_waves(chunks, (int64_t)Hkv * B);
-  const int64_t n_cg = (chunks + waves - 1) / waves;
+  // small launches: 4 query chunks per workgroup, their keys split between two wave groups
+  const bool split = attn_waves(chunks, (int64_t)Hkv * B) == 4;
+  const int per_cg = split ? 4 : 8;
+  const int64_t n_cg = (chunks + per_cg - 1) / per_cg;
   const int64_t blocks = n_cg * Hkv * B;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634073599246810019);
-  auto kern = waves == 8 ? gen_attn_bf16_kernel : gen_attn_bf16_w4_kernel;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(waves * 64), 0, stream,
+  auto kern = split ? gen_attn_bf16_split_kernel : gen_attn_bf16_kernel;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(512), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_img),
                      static_cast<const uint16_t*>(v_img), static_cast<const uint16_t*>(k_pre),
                      static_cast<const uint16_t*>(v_pre), cu_q, cu_p, Hq, Hkv, (int)n_cg,
