@@ -55,7 +55,7 @@ def assert_close(got, ref, dtype: str, what: str = ""):
 
 # Embedding front end (pixels and patch features enter the matrix cores in bf16): every
 # element within 2^-5 (|ref| + rms(ref)) and relative L2 <= 5e-3.  Two bf16 roundings (the
-# pixels, the patch features), each <= 2^-9 relative, reach an output through sums that
+# pixels, the patch features), each <= 2^-8 relative, reach an output through sums that
 # scale like the output itself; a bf16 emulation of the chain in numpy measures
 # max |err| / (|ref| + rms) ~ 1.0e-2 and rel-L2 ~ 2.4e-3 at noise scales 1 and 4, so the
 # bound leaves a factor of three.
