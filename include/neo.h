@@ -282,6 +282,7 @@ const char *neo_last_error(void);
  * transformer blocks; [B] §2.1, NEOVisionEmbeddings):
  *   neo_gen_patchify      z -> 16x16 patch rows (bf16);
  *   neo_gen_patch_embed   patch convolution + bias, GELU, interleaved two-axis rotary;
+ *   neo_gen_patch_embed_px  the two above in one launch, from the pixels;
  *   neo_gen_cond_hidden / neo_gen_cond_out   the time and noise-scale embedders ([A]
  *                         §Timestep and noise-scale conditioning), summed;
  *   neo_gen_merge_embed   2x2 stride-2 convolution + bias + the conditioning vector.
@@ -318,6 +319,20 @@ neo_status neo_gen_patchify(const float *z, int32_t B, int32_t H, int32_t W, voi
 neo_status neo_gen_patch_embed(const void *patches, int32_t B, int32_t H, int32_t W,
                                const void *w1, const float *b1, int32_t C1, float rope_theta,
                                void *h_out, void *hip_stream);
+
+/*
+ * neo_gen_patch_embed_px -- neo_gen_patchify and neo_gen_patch_embed in one launch:
+ * the same patch convolution, GELU and rotary ([A] §Vision tower), with the patch
+ * rows gathered straight from the pixels and rounded to bf16 (RNE) on their way to
+ * the matrix cores, so no patch buffer passes through memory.  The result is
+ * bit-identical to the two calls.
+ *   z        [B, 3, H, W] fp32; H, W positive multiples of 16 (<= 32768); the whole
+ *            of z below 2 GiB.
+ *   w1, b1, C1, rope_theta, h_out as for neo_gen_patch_embed.
+ */
+neo_status neo_gen_patch_embed_px(const float *z, int32_t B, int32_t H, int32_t W,
+                                  const void *w1, const float *b1, int32_t C1, float rope_theta,
+                                  void *h_out, void *hip_stream);
 
 /*
  * neo_gen_cond_hidden -- first layer of the time and noise-scale embedders:

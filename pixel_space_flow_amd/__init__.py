@@ -15,7 +15,7 @@ import os
 
 __all__ = ["qknorm_rope3", "qkv_proj_norm_rope", "gen_attn_fwd", "prefill_attn_fwd",
            "fm_euler_step",
-           "fm_euler_step_cfg", "cfg_path", "gen_patchify", "gen_patch_embed",
+           "fm_euler_step_cfg", "cfg_path", "gen_patchify", "gen_patch_embed", "gen_patch_embed_px",
            "gen_cond_embed", "gen_merge_embed", "gen_embed", "shift_time",
            "NeoError", "lib", "LIB_PATH", "EXPORTED_SYMBOLS", "NEO_OK", "NEO_ERR_NULL", "NEO_ERR_SHAPE", "NEO_ERR_VALUE",
            "NEO_ERR_UNSUPPORTED", "NEO_ERR_HIP", "NEO_F32", "NEO_BF16"]
@@ -28,6 +28,7 @@ NEO_F32, NEO_BF16 = 0, 1
 EXPORTED_SYMBOLS = ("neo_qknorm_rope3", "neo_gen_attn_fwd", "neo_fm_euler_step",
                     "neo_cfg_path", "neo_fm_euler_step_cfg", "neo_prefill_attn_fwd",
                     "neo_qkv_proj_norm_rope", "neo_gen_patchify", "neo_gen_patch_embed",
+                    "neo_gen_patch_embed_px",
                     "neo_gen_cond_hidden", "neo_gen_cond_out", "neo_gen_merge_embed",
                     "neo_shift_time", "neo_status_string", "neo_last_error")
 
@@ -75,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.neo_gen_patchify.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp]
         L.neo_gen_patch_embed.restype = ctypes.c_int
         L.neo_gen_patch_embed.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _f32, _vp, _vp]
+        L.neo_gen_patch_embed_px.restype = ctypes.c_int
+        L.neo_gen_patch_embed_px.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _f32, _vp, _vp]
         L.neo_gen_cond_hidden.restype = ctypes.c_int
         L.neo_gen_cond_hidden.argtypes = [_f32, _f32, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
         L.neo_gen_cond_out.restype = ctypes.c_int
@@ -335,6 +338,27 @@ def gen_patch_embed(patches, B, H, W, w1, b1, rope_theta=1.0e4, h_out=None):
     return h_out
 
 
+def gen_patch_embed_px(z, w1, b1, rope_theta=1.0e4, h_out=None):
+    """Patchify and the patch convolution + GELU + rotary in one launch, from the pixels:
+    z [B, 3, H, W] fp32 -> [B*P, C1] bf16 (bit-identical to gen_patchify + gen_patch_embed)."""
+    torch = _torch()
+    _dev(z, "z", torch.float32)
+    if z.dim() != 4 or z.shape[1] != 3:
+        raise ValueError(f"z must be [B, 3, H, W], got {tuple(z.shape)}")
+    B, _, H, W = z.shape
+    P = (H // 16) * (W // 16)
+    _dev(w1, "w1", torch.bfloat16)
+    C1 = w1.shape[0]
+    _dev(w1, "w1", torch.bfloat16, (C1, 768))
+    _dev(b1, "b1", torch.float32, (C1,))
+    h_out = (torch.empty((B * P, C1), dtype=torch.bfloat16, device=z.device) if h_out is None
+             else _dev(h_out, "h_out", torch.bfloat16, (B * P, C1)))
+    st = lib().neo_gen_patch_embed_px(z.data_ptr(), B, H, W, w1.data_ptr(), b1.data_ptr(), C1,
+                                      float(rope_theta), h_out.data_ptr(), _stream(z))
+    _check("neo_gen_patch_embed_px", st)
+    return h_out
+
+
 def gen_cond_embed(t, noise_scale, noise_scale_max, emb_t, emb_s, hidden=None, cond=None):
     """Time + noise-scale embedders summed -> cond [D] fp32.  emb_t, emb_s: (wa [D, 256] bf16,
     ba [D] fp32, wb [D, D] bf16, bb [D] fp32).  Two calls; hidden [2, D] fp32 holds the
@@ -385,10 +409,9 @@ def gen_merge_embed(h, B, H, W, w2, b2, cond, tokens=None):
 
 def gen_embed(z, w1, b1, w2, b2, emb_t, emb_s, t, noise_scale, noise_scale_max,
               rope_theta=1.0e4):
-    """The whole front end, z [B, 3, H, W] fp32 -> tokens [B*N, D] fp32 (five launches)."""
+    """The whole front end, z [B, 3, H, W] fp32 -> tokens [B*N, D] fp32 (four launches)."""
     B, _, H, W = z.shape
-    patches = gen_patchify(z)
-    h = gen_patch_embed(patches, B, H, W, w1, b1, rope_theta)
+    h = gen_patch_embed_px(z, w1, b1, rope_theta)
     cond, _ = gen_cond_embed(t, noise_scale, noise_scale_max, emb_t, emb_s)
     return gen_merge_embed(h, B, H, W, w2, b2, cond)
 

@@ -454,6 +454,34 @@ neo_status neo_gen_patch_embed(const void* patches, int32_t B, int32_t H, int32_
                   "neo_gen_patch_embed launch");
 }
 
+neo_status neo_gen_patch_embed_px(const float* z, int32_t B, int32_t H, int32_t W,
+                                  const void* w1, const float* b1, int32_t C1, float rope_theta,
+                                  void* h_out, void* hip_stream) {
+  const char* fn = "neo_gen_patch_embed_px";
+  if (!image_ok(B, H, W, 16))
+    return fail(NEO_ERR_SHAPE, "%s: B=%d H=%d W=%d (H, W positive multiples of 16, <= 32768)", fn, B, H, W);
+  if (C1 < 64 || C1 % 64 != 0 || C1 > 16384)
+    return fail(NEO_ERR_SHAPE, "%s: C1=%d must be a positive multiple of 64 (<= 16384)", fn, C1);
+  if (!finite(rope_theta) || rope_theta <= 1.0f)
+    return fail(NEO_ERR_VALUE, "%s: rope_theta must be finite and > 1", fn);
+  const int64_t M = (int64_t)B * (H / 16) * (W / 16);
+  const int64_t zb = (int64_t)B * 3 * H * W * 4;
+  if (zb >= ((int64_t)1 << 31))
+    return fail(NEO_ERR_SHAPE, "%s: z is %lld bytes (must be below 2 GiB)", fn, (long long)zb);
+  if (!grid_fits(neo::gemm_max_blocks(C1, M), neo::kGemmThreads))
+    return fail(NEO_ERR_SHAPE, "%s: problem too large for one launch", fn);
+  if (M == 0) return ok();
+  if (!z || !w1 || !b1 || !h_out) return fail(NEO_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (!all16({z, w1, b1, h_out})) return fail(NEO_ERR_VALUE, "%s: buffers must be 16-byte aligned", fn);
+  const size_t hb = (size_t)M * C1 * 2;
+  if (overlap(h_out, hb, z, (size_t)zb) || overlap(h_out, hb, w1, (size_t)C1 * 768 * 2) ||
+      overlap(h_out, hb, b1, (size_t)C1 * 4))
+    return fail(NEO_ERR_VALUE, "%s: h_out overlaps an input", fn);
+  return from_hip(neo::launch_gen_patch_embed_px(z, B, H, W, w1, b1, C1, (double)rope_theta, h_out,
+                                                 static_cast<hipStream_t>(hip_stream)),
+                  "neo_gen_patch_embed_px launch");
+}
+
 neo_status neo_gen_cond_hidden(float t, float noise_scale, float noise_scale_max, int32_t D,
                                const void* wa_t, const float* ba_t, const void* wa_s,
                                const float* ba_s, float* hidden, void* hip_stream) {

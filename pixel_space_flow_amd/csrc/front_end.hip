@@ -99,30 +99,13 @@ __device__ __forceinline__ float gelu(float x) {
   return 0.5f * x * (1.0f + copysignf(erf_abs, x));
 }
 
+// The epilogue of a patch-convolution tile: bias, GELU, rotary, bf16 stores.
 template <int TW>
-__device__ __forceinline__ void patch_tile(const uint16_t* __restrict__ patches,
-                                           const uint16_t* __restrict__ w1,
-                                           const float* __restrict__ b1, int64_t M, int C1,
-                                           int gw, int P, float l2f, int f0, int t0,
-                                           uint16_t* __restrict__ hout, uint8_t* lw0,
-                                           uint8_t* lw1, uint8_t* lx0, uint8_t* lx1) {
-  constexpr int kTTile = 128 * TW;
+__device__ __forceinline__ void patch_epilogue(f32x16 (&acc)[TW][4], const float* __restrict__ b1,
+                                               int64_t M, int C1, int gw, int P, float l2f,
+                                               int f0, int t0, uint16_t* __restrict__ hout) {
   const int lane = threadIdx.x & 63, hl = lane >> 5, col = lane & 31;
   const int wave = threadIdx.x >> 6, hh = wave >> 2, tg = wave & 3;
-  constexpr uint32_t kRowBytes = kPatchK * 2;
-  const int wrows = C1 - f0 < gemm::kFT ? C1 - f0 : gemm::kFT;
-  const int64_t xleft = M - t0 < 0 ? 0 : M - t0;
-  const int xrows = xleft < kTTile ? (int)xleft : kTTile;
-  const __amdgpu_buffer_rsrc_t rw = gemm::make_rsrc(w1 + (int64_t)f0 * kPatchK, (uint32_t)wrows * kRowBytes);
-  const __amdgpu_buffer_rsrc_t rx =
-      gemm::make_rsrc(patches + (int64_t)t0 * kPatchK, (uint32_t)xrows * kRowBytes);
-  f32x16 acc[TW][4];
-  gemm::mainloop<TW>(
-      acc, rw, kRowBytes, rx,
-      [&](int r) __attribute__((always_inline)) { return (uint32_t)r * kRowBytes; },
-      [&](int s) __attribute__((always_inline)) { return (uint32_t)(s * gemm::kRowB); },
-      kPatchK / gemm::kKS, lw0, lw1, lx0, lx1);
-
   // per-lane constants shared by both token columns: the bias of each feature and the
   // rotary rate (revolutions per grid step) of each feature pair
   const int half_c = C1 >> 1;
@@ -183,6 +166,31 @@ __device__ __forceinline__ void patch_tile(const uint16_t* __restrict__ patches,
   }
 }
 
+// A tile whose X rows are the bf16 patch rows of patchify_bf16_kernel.
+template <int TW>
+__device__ __forceinline__ void patch_tile(const uint16_t* __restrict__ patches,
+                                           const uint16_t* __restrict__ w1,
+                                           const float* __restrict__ b1, int64_t M, int C1,
+                                           int gw, int P, float l2f, int f0, int t0,
+                                           uint16_t* __restrict__ hout, uint8_t* lw0,
+                                           uint8_t* lw1, uint8_t* lx0, uint8_t* lx1) {
+  constexpr int kTTile = 128 * TW;
+  constexpr uint32_t kRowBytes = kPatchK * 2;
+  const int wrows = C1 - f0 < gemm::kFT ? C1 - f0 : gemm::kFT;
+  const int64_t xleft = M - t0 < 0 ? 0 : M - t0;
+  const int xrows = xleft < kTTile ? (int)xleft : kTTile;
+  const __amdgpu_buffer_rsrc_t rw = gemm::make_rsrc(w1 + (int64_t)f0 * kPatchK, (uint32_t)wrows * kRowBytes);
+  const __amdgpu_buffer_rsrc_t rx =
+      gemm::make_rsrc(patches + (int64_t)t0 * kPatchK, (uint32_t)xrows * kRowBytes);
+  f32x16 acc[TW][4];
+  gemm::mainloop<TW>(
+      acc, rw, kRowBytes, rx,
+      [&](int r) __attribute__((always_inline)) { return (uint32_t)r * kRowBytes; },
+      [&](int s) __attribute__((always_inline)) { return (uint32_t)(s * gemm::kRowB); },
+      kPatchK / gemm::kKS, lw0, lw1, lx0, lx1);
+  patch_epilogue<TW>(acc, b1, M, C1, gw, P, l2f, f0, t0, hout);
+}
+
 __global__ __launch_bounds__(kThreads, 1) void patch_gemm_kernel(
     const uint16_t* __restrict__ patches, const uint16_t* __restrict__ w1,
     const float* __restrict__ b1, int64_t M, int C1, int gw, int P, float l2f, gemm::Plan plan,
@@ -194,6 +202,82 @@ __global__ __launch_bounds__(kThreads, 1) void patch_gemm_kernel(
     patch_tile<2>(patches, w1, b1, M, C1, gw, P, l2f, tl.f0, tl.t0, hout, lw0, lw1, lx0, lx1);
   else
     patch_tile<1>(patches, w1, b1, M, C1, gw, P, l2f, tl.f0, tl.t0, hout, lw0, lw1, lx0, lx1);
+}
+
+// A tile whose X rows are gathered from the fp32 pixels and rounded to bf16 on their way
+// into LDS -- the rows patchify_bf16_kernel would write, so the result is bit-identical to
+// patchify followed by patch_tile.  K stage s covers channel s / 4 and pixel rows
+// 4 (s % 4) .. +3 of each patch; its 16-byte LDS chunk q holds pixel row q / 2, columns
+// 8 (q % 2) .. +7.  Thread t fills, for tile row r = t / (8 / (2 TW)) and column half
+// t % 2, the chunks of 2 TW consecutive pixel rows: two 16-byte loads of 8 fp32 each.  Along
+// a patch row the tile's rows are consecutive 64-byte runs of the same pixel row, so
+// consecutive lanes read consecutive 32-byte pieces.
+template <int TW>
+__device__ __forceinline__ void patch_px_tile(const float* __restrict__ z, uint32_t z_bytes,
+                                              int H, int W, const uint16_t* __restrict__ w1,
+                                              const float* __restrict__ b1, int64_t M, int C1,
+                                              int gw, int P, float l2f, int f0, int t0,
+                                              uint16_t* __restrict__ hout, uint8_t* lw0,
+                                              uint8_t* lw1, uint8_t* lx0, uint8_t* lx1) {
+  constexpr uint32_t kRowBytes = kPatchK * 2;
+  constexpr int kJ = 2 * TW;  // pixel rows per thread and stage
+  const int wrows = C1 - f0 < gemm::kFT ? C1 - f0 : gemm::kFT;
+  const __amdgpu_buffer_rsrc_t rw = gemm::make_rsrc(w1 + (int64_t)f0 * kPatchK, (uint32_t)wrows * kRowBytes);
+  const __amdgpu_buffer_rsrc_t rz = gemm::make_rsrc(z, z_bytes);
+  const int tid = threadIdx.x;
+  const int r = tid / (8 / kJ), half = tid & 1, jb = ((tid >> 1) % (4 / kJ)) * kJ;
+  // byte offset of this thread's first piece (channel 0, pixel row 0 of its patch), or past
+  // the pixels for rows beyond the last patch; every offset is below 2^31 + z_bytes < 2^32
+  uint32_t base = gemm::kAbsentRow;
+  const int64_t m = (int64_t)t0 + r;
+  if (m < M) {
+    const uint32_t b = (uint32_t)(m / P), mi = (uint32_t)(m - (int64_t)b * P);
+    const uint32_t py = mi / (uint32_t)gw, px = mi - py * (uint32_t)gw;
+    base = (((b * 3u * (uint32_t)H + 16u * py) * (uint32_t)W) + 16u * px + 8u * (uint32_t)half) * 4u;
+  }
+  const uint32_t row_b = (uint32_t)W * 4u;  // one pixel row
+  const int slot0 = r * gemm::kRowB;
+  f32x16 acc[TW][4];
+  gemm::mainloop_xreg<TW, 2 * kJ>(
+      acc, rw, kRowBytes,
+      [&](int s, uint4 (&xr)[2 * kJ]) __attribute__((always_inline)) {
+        const uint32_t so = ((uint32_t)(s >> 2) * (uint32_t)H + 4u * (uint32_t)(s & 3)) * row_b;
+#pragma unroll
+        for (int jj = 0; jj < kJ; ++jj) {
+          const uint32_t off = base + so + (uint32_t)(jb + jj) * row_b;
+          xr[2 * jj] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rz, (int)off, 0, 0));
+          xr[2 * jj + 1] =
+              __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rz, (int)(off + 16u), 0, 0));
+        }
+      },
+      [&](uint8_t* xb, const uint4 (&xr)[2 * kJ]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int jj = 0; jj < kJ; ++jj) {
+          const float4 a = __builtin_bit_cast(float4, xr[2 * jj]);
+          const float4 c = __builtin_bit_cast(float4, xr[2 * jj + 1]);
+          const int q = 2 * (jb + jj) + half;
+          *reinterpret_cast<uint4*>(xb + slot0 + ((q ^ gemm::pswz(r)) << 4)) =
+              make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(c.x, c.y),
+                         pack_bf16x2(c.z, c.w));
+        }
+      },
+      kPatchK / gemm::kKS, lw0, lw1, lx0, lx1);
+  patch_epilogue<TW>(acc, b1, M, C1, gw, P, l2f, f0, t0, hout);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void patch_px_gemm_kernel(
+    const float* __restrict__ z, uint32_t z_bytes, int H, int W,
+    const uint16_t* __restrict__ w1, const float* __restrict__ b1, int64_t M, int C1, int gw,
+    int P, float l2f, gemm::Plan plan, uint16_t* __restrict__ hout) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lw0[gemm::kWTileB], lw1[gemm::kWTileB],
+      lx0[gemm::kXTileB], lx1[gemm::kXTileB];
+  const gemm::Tile tl = gemm::tile_of(blockIdx.x, plan);
+  if (tl.full)
+    patch_px_tile<2>(z, z_bytes, H, W, w1, b1, M, C1, gw, P, l2f, tl.f0, tl.t0, hout, lw0, lw1,
+                     lx0, lx1);
+  else
+    patch_px_tile<1>(z, z_bytes, H, W, w1, b1, M, C1, gw, P, l2f, tl.f0, tl.t0, hout, lw0, lw1,
+                     lx0, lx1);
 }
 
 // ---- time and noise-scale embedders ----------------------------------------------------
@@ -392,6 +476,22 @@ hipError_t launch_gen_patch_embed(const void* patches, int B, int H, int W, cons
                      dim3(kThreads), 0, stream, static_cast<const uint16_t*>(patches),
                      static_cast<const uint16_t*>(w1), b1, M, C1, gw, P, l2f, plan,
                      static_cast<uint16_t*>(h));
+  return hipGetLastError();
+}
+
+hipError_t launch_gen_patch_embed_px(const float* z, int B, int H, int W, const void* w1,
+                                     const float* b1, int C1, double theta, void* h,
+                                     hipStream_t stream) {
+  const int gw = W / kPatch;
+  const int P = (H / kPatch) * gw;
+  const int64_t M = (int64_t)B * P;
+  if (M == 0) return hipSuccess;
+  const gemm::Plan plan = gemm::make_plan(C1, M);
+  const float l2f = (float)(2.0 * log2(theta) / (C1 / 2));
+  const uint32_t z_bytes = (uint32_t)((int64_t)B * 3 * H * W * 4);
+  hipLaunchKernelGGL(patch_px_gemm_kernel, dim3((unsigned)(plan.n_full + plan.n_half)),
+                     dim3(kThreads), 0, stream, z, z_bytes, H, W, static_cast<const uint16_t*>(w1),
+                     b1, M, C1, gw, P, l2f, plan, static_cast<uint16_t*>(h));
   return hipGetLastError();
 }
 

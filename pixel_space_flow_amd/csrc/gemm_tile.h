@@ -223,5 +223,101 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[TW][4], __amdgpu_buffer_r
   }
 }
 
+// ---- the main loop with X built in registers ---------------------------------------------
+// For an X that is not stored as bf16 rows (the patch convolution reads fp32 pixels): the
+// caller's xload(s, xr) issues this thread's global loads of stage s into xr (kXR 16-byte
+// registers), and xstore(xbuf, xr) converts them and writes them into an X tile buffer in
+// the layout the fragment reads expect (row r, 16-byte chunk c in slot c ^ pswz(r)).  W rows
+// arrive by LDS-direct loads as in mainloop.  Stage s + 1's X is loaded into registers
+// during stage s - 1 and written to LDS during stage s, after the first k-step's products,
+// into the buffer every wave finished reading at the barrier before; the products are
+// those of mainloop, in the same order, so the sums are bit-identical to mainloop's on the
+// same bf16 rows.
+template <int TW, int kXR, class XLoad, class XStore>
+__device__ __forceinline__ void mainloop_xreg(f32x16 (&acc)[TW][4], __amdgpu_buffer_rsrc_t rw,
+                                              uint32_t w_row_bytes, XLoad xload, XStore xstore,
+                                              int S, uint8_t* lw0, uint8_t* lw1, uint8_t* lx0,
+                                              uint8_t* lx1) {
+  auto wbuf = [&](int b) __attribute__((always_inline)) -> uint8_t* { return b == 0 ? lw0 : lw1; };
+  auto xbuf = [&](int b) __attribute__((always_inline)) -> uint8_t* { return b == 0 ? lx0 : lx1; };
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, hl = lane >> 5, col = lane & 31;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int hh = wave >> 2, tg = wave & 3;
+
+  // W staging as in mainloop: wave w loads W blocks 4w .. 4w+3
+  int wofs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * (4 * wave + i) + (lane >> 3);
+    wofs[i] = row * (int)w_row_bytes + (((lane & 7) ^ pswz(row)) << 4);
+  }
+  auto load_w = [&](int s, int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rw, (__attribute__((address_space(3))) void*)(wbuf(b) + (4 * wave_u + i) * 1024), 16,
+          wofs[i] + s * kRowB, 0, 0, 0);
+  };
+
+  int ofs[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) ofs[kk] = col * kRowB + (((2 * kk + hl) ^ pswz(col)) << 4);
+  const int wrow0 = hh * 128 * kRowB, xrow0 = tg * 32 * TW * kRowB;
+
+#pragma unroll
+  for (int ti = 0; ti < TW; ++ti)
+#pragma unroll
+    for (int fi = 0; fi < 4; ++fi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[ti][fi][r] = 0.0f;
+
+  uint4 xr[kXR];
+  load_w(0, 0);
+  xload(0, xr);
+  xstore(xbuf(0), xr);
+  if (1 < S) xload(1, xr);
+  __syncthreads();
+
+  auto stage = [&](int s, auto s2) __attribute__((always_inline)) {
+    constexpr int B = decltype(s2)::value;
+    if (s + 1 < S) load_w(s + 1, B ^ 1);
+    const uint8_t* wb = wbuf(B) + wrow0;
+    const uint8_t* xb = xbuf(B) + xrow0;
+    bf16x8 af[2][4], bf[2][TW];
+    auto fetch = [&](int kk, int slot) __attribute__((always_inline)) {
+#pragma unroll
+      for (int ti = 0; ti < TW; ++ti)
+        bf[slot][ti] = as_bf16x8(*reinterpret_cast<const uint4*>(xb + ti * 32 * kRowB + ofs[kk]));
+#pragma unroll
+      for (int fi = 0; fi < 4; ++fi)
+        af[slot][fi] = as_bf16x8(*reinterpret_cast<const uint4*>(wb + fi * 32 * kRowB + ofs[kk]));
+    };
+    fetch(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk + 1 < 4) fetch(kk + 1, (kk + 1) & 1);
+      if (kk == 1 && s + 1 < S) {
+        xstore(xbuf(B ^ 1), xr);
+        if (s + 2 < S) xload(s + 2, xr);
+      }
+#pragma unroll
+      for (int ti = 0; ti < TW; ++ti)
+#pragma unroll
+        for (int fi = 0; fi < 4; ++fi)
+          acc[ti][fi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][fi], bf[kk & 1][ti],
+                                                                acc[ti][fi], 0, 0, 0);
+    }
+    __syncthreads();
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  for (int s = 0; s < S; s += 2) {
+    stage(s, C0{});
+    if (s + 1 >= S) break;
+    stage(s + 1, C1{});
+  }
+}
+
 }  // namespace gemm
 }  // namespace neo

@@ -57,6 +57,9 @@ hipError_t launch_gen_patchify(const float* z, int B, int H, int W, void* patche
 hipError_t launch_gen_patch_embed(const void* patches, int B, int H, int W, const void* w1,
                                   const float* b1, int C1, double theta, void* h,
                                   hipStream_t stream);
+hipError_t launch_gen_patch_embed_px(const float* z, int B, int H, int W, const void* w1,
+                                     const float* b1, int C1, double theta, void* h,
+                                     hipStream_t stream);
 hipError_t launch_gen_cond_hidden(float arg_t, float arg_s, int D, const void* wa_t,
                                   const float* ba_t, const void* wa_s, const float* ba_s,
                                   float* hidden, hipStream_t stream);

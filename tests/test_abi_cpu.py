@@ -295,6 +295,9 @@ def _fe(L, fn, **kw):
     if fn == "patch":
         return L.neo_gen_patch_embed(d["p"], d["B"], d["H"], d["Wd"], d["w1"], d["b1"], d["C1"],
                                      d["th"], d["h"], None)
+    if fn == "patchpx":
+        return L.neo_gen_patch_embed_px(d["z"], d["B"], d["H"], d["Wd"], d["w1"], d["b1"], d["C1"],
+                                        d["th"], d["h"], None)
     if fn == "hidden":
         return L.neo_gen_cond_hidden(d["t"], d["ns"], d["nsm"], d["D"], d["wa_t"], d["ba_t"],
                                      d["wa_s"], d["ba_s"], d["hid"], None)
@@ -321,6 +324,13 @@ def _fe(L, fn, **kw):
     ("patch", dict(b1=None), P.NEO_ERR_NULL),
     ("patch", dict(h=FAKE + (1 << 30) + 64), P.NEO_ERR_VALUE),   # h overlaps the patches
     ("patch", dict(B=1 << 16, H=1 << 15, Wd=1 << 15), P.NEO_ERR_SHAPE),  # grid too large
+    ("patchpx", dict(H=40), P.NEO_ERR_SHAPE),                   # not a multiple of 16
+    ("patchpx", dict(C1=100), P.NEO_ERR_SHAPE),
+    ("patchpx", dict(B=4, H=8192, Wd=8192), P.NEO_ERR_SHAPE),   # z reaches 2 GiB
+    ("patchpx", dict(th=0.5), P.NEO_ERR_VALUE),
+    ("patchpx", dict(z=None), P.NEO_ERR_NULL),
+    ("patchpx", dict(w1=FAKE + (2 << 30) + 8), P.NEO_ERR_VALUE),  # misaligned
+    ("patchpx", dict(h=FAKE + 4096), P.NEO_ERR_VALUE),          # h overlaps z
     ("hidden", dict(D=100), P.NEO_ERR_SHAPE),                   # not a multiple of 8
     ("hidden", dict(nsm=0.0), P.NEO_ERR_VALUE),
     ("hidden", dict(t=math.nan), P.NEO_ERR_VALUE),
@@ -345,6 +355,7 @@ def test_front_end_validation(L, fn, kw, status):
 def test_front_end_empty_is_ok(L):
     assert _fe(L, "patchify", B=0, z=None) == P.NEO_OK
     assert _fe(L, "patch", B=0, p=None) == P.NEO_OK
+    assert _fe(L, "patchpx", B=0, z=None) == P.NEO_OK
     assert _fe(L, "merge", B=0, h=None) == P.NEO_OK
 
 

@@ -123,6 +123,30 @@ def test_patch_embed(neo, B, Hh, Ww, C1):
     H.assert_front_end(H.host(h).reshape(ref.shape), ref, f"patch embed {z.shape} C1={C1}")
 
 
+@pytest.mark.parametrize("B,Hh,Ww,C1", [(1, 256, 256, 1024), (2, 64, 96, 192), (1, 32, 32, 64),
+                                         (3, 160, 48, 320), (1, 2080, 2048, 1024)])
+def test_patch_embed_px(neo, B, Hh, Ww, C1):
+    """The one-launch form from the pixels: every bit equal to patchify followed by the
+    patch convolution (the same RNE rounding of the same pixels, the same products in the
+    same order), on pixels that are not bf16-exact; 2080 x 2048 gives 260 tiles, so half
+    tiles run too.  The smaller shapes are also compared with the oracle on the rounded
+    pixels."""
+    torch = _cuda()
+    rng = np.random.default_rng(C1 + Hh + 7)
+    z = (2.0 * rng.standard_normal((B, 3, Hh, Ww))).astype(np.float32)
+    w1, b1, _, _ = _weights(rng, C1, 32)
+    _say(f"patch embed from pixels z {z.shape} C1={C1}")
+    zd, w1d, b1d = H.dev_f32(z), H.dev(w1.reshape(C1, -1), "bf16"), H.dev_f32(b1)
+    h_px = neo.gen_patch_embed_px(zd, w1d, b1d)
+    h_two = neo.gen_patch_embed(neo.gen_patchify(zd), B, Hh, Ww, w1d, b1d)
+    torch.cuda.synchronize()
+    assert torch.equal(h_px.view(torch.int16), h_two.view(torch.int16)), "differs from the two calls"
+    if Hh * Ww <= 256 * 256:
+        zr = W.bf16_round(z)
+        ref = fe.rope2d_interleaved(fe.gelu(fe.patch_conv(zr, w1, b1)), Hh // 16, Ww // 16)
+        H.assert_front_end(H.host(h_px).reshape(ref.shape), ref, f"patch embed px {z.shape} C1={C1}")
+
+
 @pytest.mark.parametrize("D,t,ns", [(4096, 0.35, 4.0), (96, 0.0, 1.0), (512, 0.95, 16.0)])
 def test_cond_embed(neo, D, t, ns):
     """Both embedders, summed: fp32 results of bf16 weights against fp64."""
