@@ -148,7 +148,7 @@ __device__ __forceinline__ void patch_epilogue(f32x16 (&acc)[TW][4], const float
           v[e] = gelu(x);
         }
         // pairs (f, f + 1), f even: elements e = 0, 1 and 2, 3.  The angle is taken in
-        // revolutions and reduced to quarter turns inside sincos_turns, which needs no wide
+        // revolutions and reduced to one turn inside sincos_turns, which needs no wide
         // argument reduction (positions are below 2^11, so the fp32 revolutions carry an
         // absolute error under 1e-4 turn at the largest image and ~1e-6 at 2048 px).
 #pragma unroll
