@@ -409,20 +409,26 @@ def main():
     # events are read only after the timed steps, so the device runs without a pause from
     # the warm-up to the end of the timed steps (a pause of a few ms restarts the clock
     # transient described at WARM_MS).
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
     pc_events = per_call_enqueue(step, a.calls) if a.calls > 0 else None
     for i in range(a.warmup):
         step(i)
 
     # the benchmark proper: W untimed steps (above), then exactly K steps between two
-    # synchronisations
+    # synchronisations.  No event is recorded inside them: an event record between two
+    # kernels adds its own dispatch to the stream (about 4% of a step in same-box runs).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(a.steps):
-        step(i, events[i])
+        step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / a.steps
+    # the same K steps once more, each kernel between its own events, for the per-kernel
+    # durations of the steps as timed (queued back to back, read after the stream drains)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    for i in range(a.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
     steps_us = {"qknorm_rope3": stats_us([e[0].elapsed_time(e[1]) for e in events]),
                 "gen_attn": stats_us([e[1].elapsed_time(e[2]) for e in events]),
                 "fm_euler_step": stats_us([e[2].elapsed_time(e[3]) for e in events])}
@@ -661,6 +667,7 @@ def main():
                                   f"launch stream; roofline.achieved uses the attention's mean, "
                                   f"the rates the medians"),
                      "kernels_us": kus},
+        # K more steps right after the timed ones, each kernel between its own events
         "timed_steps_kernels_us": steps_us,
         "kernels_us": {"qknorm_rope3": pro_us, "gen_attn": att_us, "fm_euler_step": eul_us},
         "hbm_gbs": {"qknorm_rope3": fig["prologue_gbs"], "fm_euler_step": fig["euler_gbs"]},
