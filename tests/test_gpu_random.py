@@ -4,8 +4,10 @@ The other GPU tests pick their shapes by hand (the five workloads, edges, launch
 Here each case draws its shape from a fixed seed: a ragged batch of 1-6 samples with
 0-640 image tokens and 0-640 prefix tokens each (both attention launch forms occur), one
 of several head groupings (G = 1, 2, 3, 4, 8), bf16 or fp32, score scales from flat to
-peaky; prologue row counts, scales and positions, in place or not; Euler lengths and
-offsets; prefill layouts of text and image runs.  Every case prints its
+peaky; prologue row counts, scales and positions, in place or not; Euler and guided Euler
+lengths, offsets, scales and intervals; prefill layouts of text and image runs; fused
+projection token counts, widths and head groups; whole front ends of several image sizes
+and widths.  Every case prints its
 parameters before it runs and is held to the same bounds as the hand-picked ones: fp32
 max-abs 1e-4; bf16 max-abs 2e-2 and relative L2 5e-3; log-sum-exp as in test_gpu_parity.
 """
@@ -151,3 +153,76 @@ def test_random_prefill(neo, seed):
     ref, ref_lse = oracle.prefill_attn(qb, kb, vb, d["idx"], d["cu"], with_lse=True)
     H.assert_close(H.host(out), ref, "bf16", f"random prefill {seed}")
     _check_lse(H.host(lse).T, ref_lse, "bf16", f"random prefill {seed}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_cfg_euler(neo, seed):
+    import torch
+    rng = np.random.default_rng([seed, 0x6366])
+    n = int(rng.integers(1, 200000))
+    off = int(rng.integers(0, 4))
+    t = float(rng.uniform(0.0, 1.0))
+    tn = float(min(1.0, t + rng.uniform(0.0, 0.2)))
+    g = float(rng.choice([1.0, 2.0, 4.0, 7.5]))
+    gi = float(rng.choice([1.0, 1.5, 2.0]))
+    iv = (0.0, 1.0)  # the whole trajectory guided, or a drawn interval
+    if rng.random() < 0.5:
+        iv = tuple(sorted(float(x) for x in rng.uniform(0, 1, 2)))
+    path = neo.cfg_path(t, g, gi, iv)
+    _say(f"cfg euler seed={seed} n={n} offset={off} t={t:.4f} t_next={tn:.4f} gamma={g} "
+         f"gamma_img={gi} interval={iv} path={path}")
+    z0, xc, xtu, xu = (rng.standard_normal(n + off).astype(np.float32) for _ in range(4))
+    d = [H.dev_f32(a) for a in (z0, xc, xtu, xu)]
+    # branches the path does not read are passed as None
+    args = [d[1][off:], d[2][off:] if path in (2, 4) else None,
+            d[3][off:] if path in (3, 4) else None]
+    neo.fm_euler_step_cfg(d[0][off:], *args, t=t, t_next=tn, cfg_scale=g, img_cfg_scale=gi,
+                          cfg_interval=iv)
+    torch.cuda.synchronize()
+    assert path == oracle.cfg_path(np.float32(t), g, gi, iv)
+    ref = oracle.euler_step_cfg(z0[off:], xc[off:], xtu[off:], xu[off:], t=t, t_next=tn,
+                                cfg_scale=g, img_cfg_scale=gi, cfg_interval=iv)
+    got = H.host(d[0])
+    H.assert_close(got[off:], ref, "f32", f"random cfg euler {seed}")
+    assert np.array_equal(got[:off], z0[:off]), "guided step wrote before its start"
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_random_projection(neo, seed):
+    import torch
+    import workloads as W
+    rng = np.random.default_rng([seed, 0x716b])
+    N = int(rng.integers(1, 701))
+    hidden = 64 * int(rng.integers(1, 17))
+    Hq, Hkv = [(1, 1), (3, 1), (4, 2), (6, 3), (8, 2), (12, 4)][int(rng.integers(0, 6))]
+    _say(f"projection seed={seed} N={N} hidden={hidden} Hq={Hq} Hkv={Hkv}")
+    x = W.bf16_round(rng.standard_normal((N, hidden)).astype(np.float32))
+    wq = W.bf16_round((rng.standard_normal(((Hq + 2 * Hkv) * 128, hidden)) /
+                       np.sqrt(hidden)).astype(np.float32))
+    nw = tuple(rng.uniform(0.5, 1.5, 64).astype(np.float32) for _ in range(4))
+    pos = np.stack([np.full(N, int(rng.integers(0, 20001))), rng.integers(0, 64, N),
+                    rng.integers(0, 64, N)]).astype(np.int32)
+    q, k, v = neo.qkv_proj_norm_rope(H.dev(x, "bf16"), H.dev(wq, "bf16"), Hq, Hkv,
+                                     *[H.dev_f32(a) for a in nw], H.dev_i32(pos), 5e6, 1e4, 1e-6)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.qkv_proj_norm_rope(x, wq, Hq, Hkv, *nw, pos, 5e6, 1e4, 1e-6)
+    H.assert_close(H.host(q), rq, "bf16", f"random projection q {seed}")
+    H.assert_close(H.host(k), rk, "bf16", f"random projection k {seed}")
+    H.assert_close(H.host(v), rv, "bf16", f"random projection v {seed}")
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_front_end(neo, seed):
+    from tests.test_gpu_front_end import _chain, _emb, _weights
+    rng = np.random.default_rng([seed, 0x6665])
+    B = int(rng.integers(1, 4))
+    Hh, Ww = 32 * int(rng.integers(1, 9)), 32 * int(rng.integers(1, 9))
+    C1 = 64 * int(rng.integers(1, 5))
+    D = 32 * int(rng.integers(1, 11))
+    z = (float(rng.choice([0.5, 2.0, 8.0])) * rng.standard_normal((B, 3, Hh, Ww))).astype(np.float32)
+    w1, b1, w2, b2 = _weights(rng, C1, D)
+    emb_t, emb_s = _emb(rng, D)
+    t = float(rng.uniform(0.0, 1.0))
+    ns = float(rng.uniform(1.0, 16.0))
+    _chain(neo, z, w1, b1, w2, b2, emb_t, emb_s, t, ns, 16.0,
+           f"seed={seed} B={B} {Hh}x{Ww} C1={C1} D={D}")
